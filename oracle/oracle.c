@@ -1,0 +1,325 @@
+/*
+ * oracle.c -- plain, slow CPU reference for the float8 MoE quantization path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path links, loads or calls
+ * this file; only the tests, the smoke check and the CPU-baseline leg of the
+ * benchmark do.  It shares no code, header, table or constant with the HIP
+ * library: every value below is computed from the definitions, in double
+ * precision where the arithmetic is exact and in IEEE binary32 exactly where the
+ * group-scaling definition fixes binary32 (its scales are fp32).
+ *
+ * Sources (the pages this follows):
+ *   [A2A]  "[mxfp8 MoE training] Support mxfp8 all to all in expert parallel"
+ *          (torchtitan PR 1765), Summary: the payload is quantized to mxfp8,
+ *          e4m3 data and e8m0 scales are exchanged, then dequantized back to the
+ *          original precision.
+ *   [GRP]  "[moe training] fix uncoalesced global accesses in per group rowwise
+ *          scaling kernel" (torchao PR 2761), Summary: per-group float8 scaling
+ *          whose output feeds the LHS of a scaled grouped GEMM, written row-major
+ *          or column-major (then transformed).
+ *   MXFP8 itself is the OCP Microscaling (MX) v1.0 format that the name refers
+ *   to: blocks of 32 elements share one E8M0 power-of-two scale whose exponent
+ *   is floor(log2(amax)) minus the element format's largest exponent (8 for
+ *   E4M3); elements are E4M3 (OCP "fn" variant: bias 7, max 448, NaN = S.1111.111).
+ *
+ * Readings where the pages are silent (all are also listed with the design
+ * notes of the repository):
+ *   - block of 32 contiguous elements along the last dimension;
+ *   - round-to-nearest, ties to even, saturating to +-448; signs kept (-0 stays);
+ *   - scale exponent clamped to [-127, 127]; an all-zero or subnormal block
+ *     gets code 0; a block holding Inf or NaN gets scale 0xFF and payload 0x7F;
+ *   - dequantized values are rounded once (RNE) to bf16, subnormals kept,
+ *     NaN written as 0x7FC0;
+ *   - group scaling: s = 448 / max(amax, 1e-12) in fp32, q = e4m3(fp32(x*s)),
+ *     the fp32 multiplier s is the stored scale; a column with Inf/NaN gets
+ *     s = NaN and payload 0x7F; group g spans rows [end(g-1), end(g)) with the
+ *     end offsets clamped to be non-decreasing and <= M; rows past the last end
+ *     get 0x00.
+ *
+ * Build: gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math -fPIC -shared
+ * (x86-64 SSE arithmetic: binary32 ops are correctly rounded, no x87 excess
+ * precision).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#define ORACLE_ABI 1
+
+int oracle_abi_version(void) { return ORACLE_ABI; }
+
+/* ---------------------------------------------------------------- bf16 ---- */
+
+/* Value of a bf16 bit pattern (the upper half of a binary32). */
+double oracle_bf16_value(uint16_t bits)
+{
+    uint32_t w = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &w, sizeof f);
+    return (double)f;
+}
+
+static int is_finite_d(double v) { return !isnan(v) && !isinf(v); }
+
+/* floor(log2(a)) for finite a > 0, exact (frexp returns a = f * 2^e, f in [0.5, 1)). */
+static int floor_log2(double a)
+{
+    int e;
+    (void)frexp(a, &e);
+    return e - 1;
+}
+
+/* Round a finite or infinite double once to bf16 (8 significant bits, exponent
+ * range of binary32), ties to even, subnormals kept, overflow to Inf.
+ * NaN becomes the canonical 0x7FC0. */
+uint16_t oracle_bf16_round(double v)
+{
+    if (isnan(v)) return 0x7FC0;
+    uint16_t sign = signbit(v) ? 0x8000 : 0x0000;
+    double a = fabs(v);
+    if (isinf(a)) return sign | 0x7F80;
+    if (a == 0.0) return sign;
+    int ex = floor_log2(a);
+    if (ex < -126) ex = -126;                 /* subnormal binade shares 2^-133 spacing */
+    double quantum = ldexp(1.0, ex - 7);      /* 7 stored mantissa bits */
+    double r = rint(a / quantum) * quantum;   /* a/quantum is exact; rint = ties-to-even */
+    if (r >= ldexp(1.0, 128)) return sign | 0x7F80;
+    if (r < ldexp(1.0, -126)) {               /* subnormal: r = m * 2^-133 */
+        return sign | (uint16_t)(r / ldexp(1.0, -133));
+    }
+    int e = floor_log2(r);
+    uint16_t mant = (uint16_t)((r / ldexp(1.0, e) - 1.0) * 128.0);
+    return sign | (uint16_t)((e + 127) << 7) | mant;
+}
+
+/* ---------------------------------------------------------------- e4m3 ---- */
+
+/* Decode an OCP E4M3 ("fn") code: S.EEEE.MMM, bias 7; E=0 is subnormal
+ * (m/8 * 2^-6); S.1111.111 is NaN; there is no infinity. */
+double oracle_e4m3_decode(uint8_t code)
+{
+    int s = code >> 7, E = (code >> 3) & 0xF, m = code & 0x7;
+    if (E == 15 && m == 7) return NAN;
+    double mag = (E == 0) ? ldexp((double)m / 8.0, -6) : ldexp(1.0 + (double)m / 8.0, E - 7);
+    return s ? -mag : mag;
+}
+
+/* Nearest E4M3 magnitude to a >= 0 (finite), ties to even, saturated to 448. */
+static double e4m3_round_magnitude(double a)
+{
+    if (a == 0.0) return 0.0;
+    int ex = floor_log2(a);
+    if (ex < -6) ex = -6;                     /* subnormals share the 2^-9 spacing */
+    double quantum = ldexp(1.0, ex - 3);      /* 3 stored mantissa bits */
+    double r = rint(a / quantum) * quantum;
+    if (r > 448.0) r = 448.0;                 /* saturate (480 and up are not E4M3 values) */
+    return r;
+}
+
+/* Bit pattern of an exact, non-negative E4M3 magnitude. */
+static uint8_t e4m3_magnitude_bits(double r)
+{
+    if (r == 0.0) return 0;
+    if (r < ldexp(1.0, -6)) return (uint8_t)(r / ldexp(1.0, -9));  /* subnormal: m * 2^-9 */
+    int e = floor_log2(r);
+    uint8_t mant = (uint8_t)((r / ldexp(1.0, e) - 1.0) * 8.0);
+    return (uint8_t)(((e + 7) << 3) | mant);
+}
+
+/* Encode a finite double to E4M3: round to nearest, ties to even, saturate to
+ * +-448, sign copied (so -0 and small negatives give 0x80). */
+uint8_t oracle_e4m3_encode(double y)
+{
+    uint8_t sign = signbit(y) ? 0x80 : 0x00;
+    if (isnan(y)) return 0x7F;
+    double a = fabs(y);
+    if (isinf(a)) return sign | 0x7E;         /* saturating */
+    return sign | e4m3_magnitude_bits(e4m3_round_magnitude(a));
+}
+
+/* ---------------------------------------------------------------- e8m0 ---- */
+
+/* E8M0 scale: 2^(c - 127); 0xFF is NaN. */
+double oracle_e8m0_decode(uint8_t code)
+{
+    if (code == 0xFF) return NAN;
+    return ldexp(1.0, (int)code - 127);
+}
+
+/* ------------------------------------------------------------- MXFP8 ------ */
+
+/* Shared exponent of one block of n values: floor(log2(amax)) - 8, clamped to
+ * [-127, 127] (amax = 0 counts as -infinity and clamps to -127).  Returns the
+ * E8M0 code, or 0xFF if the block holds Inf or NaN. */
+static uint8_t mx_block_scale_code(const double* v, int n)
+{
+    double amax = 0.0;
+    for (int i = 0; i < n; ++i) {
+        if (!is_finite_d(v[i])) return 0xFF;
+        double a = fabs(v[i]);
+        if (a > amax) amax = a;
+    }
+    int shared = (amax == 0.0) ? -127 : floor_log2(amax) - 8;
+    if (shared < -127) shared = -127;
+    if (shared > 127) shared = 127;
+    return (uint8_t)(shared + 127);
+}
+
+/* MX quantize one element given its block's scale code (finite block). */
+uint8_t oracle_mx_encode_element(uint16_t xbits, uint8_t scale_code)
+{
+    double x = oracle_bf16_value(xbits);
+    double y = x / ldexp(1.0, (int)scale_code - 127);  /* exact: power-of-two divide */
+    return oracle_e4m3_encode(y);
+}
+
+/* X: (M, K) bf16 bits, row-major, K % 32 == 0.
+ * Q: (M, K) E4M3 codes, row-major.  S: (M, K/32) E8M0 codes, row-major. */
+void oracle_mx_quantize(const uint16_t* x, int64_t M, int64_t K, uint8_t* q, uint8_t* s)
+{
+    const int64_t nb = K / 32;
+    double v[32];
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t b = 0; b < nb; ++b) {
+            const uint16_t* xb = x + m * K + b * 32;
+            for (int i = 0; i < 32; ++i) v[i] = oracle_bf16_value(xb[i]);
+            uint8_t c = mx_block_scale_code(v, 32);
+            s[m * nb + b] = c;
+            uint8_t* qb = q + m * K + b * 32;
+            if (c == 0xFF) {
+                for (int i = 0; i < 32; ++i) qb[i] = 0x7F;
+                continue;
+            }
+            double scale = oracle_e8m0_decode(c);
+            for (int i = 0; i < 32; ++i) qb[i] = oracle_e4m3_encode(v[i] / scale);
+        }
+    }
+}
+
+/* Dequantize one element: round_bf16(e4m3(q) * 2^(c-127)); NaN code or NaN
+ * scale gives 0x7FC0. */
+uint16_t oracle_mx_decode_element(uint8_t q, uint8_t scale_code)
+{
+    double d = oracle_e4m3_decode(q);
+    double sc = oracle_e8m0_decode(scale_code);
+    if (isnan(d) || isnan(sc)) return 0x7FC0;
+    return oracle_bf16_round(d * sc);         /* product is exact in double */
+}
+
+void oracle_mx_dequantize(const uint8_t* q, const uint8_t* s, int64_t M, int64_t K, uint16_t* y)
+{
+    const int64_t nb = K / 32;
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t k = 0; k < K; ++k)
+            y[m * K + k] = oracle_mx_decode_element(q[m * K + k], s[m * nb + k / 32]);
+}
+
+/* ------------------------------------------------------ group scaling ----- */
+
+/* binary32 helpers: every operation here is one correctly rounded IEEE op. */
+static float f32_of_bf16(uint16_t bits)
+{
+    uint32_t w = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &w, sizeof f);
+    return f;
+}
+
+/* Scale of one (group, column): s = 448 / max(amax, 1e-12) in binary32. */
+float oracle_group_scale_value(float amax)
+{
+    volatile float denom = amax > 1e-12f ? amax : 1e-12f;
+    volatile float s = 448.0f / denom;
+    return s;
+}
+
+/* Quantize one element of a group column with multiplier s (finite):
+ * the binary32 product is rounded first, then encoded to E4M3. */
+uint8_t oracle_group_encode_element(uint16_t xbits, float s)
+{
+    volatile float p = f32_of_bf16(xbits) * s;
+    return oracle_e4m3_encode((double)p);
+}
+
+/* X: (M, K) bf16 bits row-major.  group_end: G cumulative end offsets.
+ * layout 0: Q[m*K + k] (same layout as X); layout 1: Q[k*M + m].
+ * scales: (G, K) binary32, the multiplier applied before the cast. */
+void oracle_group_scale(const uint16_t* x, int64_t M, int64_t K,
+                        const int32_t* group_end, int32_t G, int layout,
+                        uint8_t* q, float* scales)
+{
+    int64_t start = 0;
+    for (int32_t g = 0; g < G; ++g) {
+        int64_t end = group_end[g];
+        if (end < start) end = start;
+        if (end > M) end = M;
+        for (int64_t k = 0; k < K; ++k) {
+            double amax = 0.0;
+            int finite = 1;
+            for (int64_t r = start; r < end; ++r) {
+                double v = oracle_bf16_value(x[r * K + k]);
+                if (!is_finite_d(v)) finite = 0;
+                else if (fabs(v) > amax) amax = fabs(v);
+            }
+            float s;
+            if (!finite) {
+                uint32_t nanbits = 0x7FC00000u;
+                memcpy(&s, &nanbits, sizeof s);
+            } else {
+                s = oracle_group_scale_value((float)amax);   /* amax is a bf16 value: exact */
+            }
+            scales[(int64_t)g * K + k] = s;
+            for (int64_t r = start; r < end; ++r) {
+                uint8_t c = finite ? oracle_group_encode_element(x[r * K + k], s) : 0x7F;
+                if (layout == 0) q[r * K + k] = c;
+                else q[k * M + r] = c;
+            }
+        }
+        start = end;
+    }
+    /* rows outside every group */
+    for (int64_t r = start; r < M; ++r)
+        for (int64_t k = 0; k < K; ++k) {
+            if (layout == 0) q[r * K + k] = 0;
+            else q[k * M + r] = 0;
+        }
+}
+
+/* ------------------------------------------------------------ transpose --- */
+
+/* out (C, R) = transpose of in (R, C), bytes. */
+void oracle_transpose_u8(const uint8_t* in, int64_t R, int64_t C, uint8_t* out)
+{
+    for (int64_t i = 0; i < R; ++i)
+        for (int64_t j = 0; j < C; ++j)
+            out[j * R + i] = in[i * C + j];
+}
+
+/* ------------------------------------------- element-wise array forms ----- */
+/* Same functions as above, applied element by element over arrays (so that
+ * exhaustive checks need not cross the FFI once per element). */
+
+void oracle_mx_encode_elements(const uint16_t* x, const uint8_t* scale_code, int64_t n, uint8_t* out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_mx_encode_element(x[i], scale_code[i]);
+}
+
+void oracle_mx_decode_elements(const uint8_t* q, const uint8_t* scale_code, int64_t n, uint16_t* out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_mx_decode_element(q[i], scale_code[i]);
+}
+
+void oracle_e4m3_encode_f32_array(const float* y, int64_t n, uint8_t* out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_e4m3_encode((double)y[i]);
+}
+
+void oracle_bf16_round_f64_array(const double* v, int64_t n, uint16_t* out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_bf16_round(v[i]);
+}
+
+void oracle_group_encode_elements(const uint16_t* x, const float* s, int64_t n, uint8_t* out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_group_encode_element(x[i], s[i]);
+}

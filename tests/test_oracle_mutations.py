@@ -1,0 +1,47 @@
+"""Plant plausible mistakes in a scratch copy of the oracle (CPU only) and check
+that the pin battery catches every one of them.  The committed oracle is never
+modified; each mutant is compiled into a temporary directory."""
+import os
+
+import pytest
+
+import oracle
+import oracle_pins as P
+
+# (id, exact text in oracle.c, replacement)
+MUTATIONS = [
+    ("e4m3_mantissa_width", "double quantum = ldexp(1.0, ex - 3);", "double quantum = ldexp(1.0, ex - 2);"),
+    ("e4m3_no_saturation", "if (r > 448.0) r = 448.0;", ""),
+    ("e4m3_ties_away", "double r = rint(a / quantum) * quantum;\n    if (r > 448.0)",
+     "double r = round(a / quantum) * quantum;\n    if (r > 448.0)"),
+    ("e4m3_subnormal_range", "if (ex < -6) ex = -6;", "if (ex < -7) ex = -7;"),
+    ("e4m3_negative_zero_lost", "uint8_t sign = signbit(y) ? 0x80 : 0x00;", "uint8_t sign = (y < 0) ? 0x80 : 0x00;"),
+    ("mx_emax_off_by_one", "floor_log2(amax) - 8;", "floor_log2(amax) - 7;"),
+    ("mx_no_low_clamp", "if (shared < -127) shared = -127;", "if (shared < -200) shared = -200;"),
+    ("mx_inf_not_poisoning", "if (!is_finite_d(v[i])) return 0xFF;", "if (isnan(v[i])) return 0xFF;"),
+    ("mx_scale_index_transposed", "s[m * nb + b] = c;", "s[b * M + m] = c;"),
+    ("mx_dequant_scale_index", "s[m * nb + k / 32]", "s[m * nb + k % nb]"),
+    ("bf16_no_subnormal_binade", "if (ex < -126) ex = -126;", ""),
+    ("bf16_ties_away", "double r = rint(a / quantum) * quantum;   /* a/quantum is exact; rint = ties-to-even */",
+     "double r = round(a / quantum) * quantum;"),
+    ("e8m0_nan_code_finite", "if (code == 0xFF) return NAN;", ""),
+    ("group_fnuz_max", "volatile float s = 448.0f / denom;", "volatile float s = 240.0f / denom;"),
+    ("group_single_rounding", "volatile float p = f32_of_bf16(xbits) * s;",
+     "volatile double p = (double)f32_of_bf16(xbits) * (double)s;"),
+    ("group_col_layout_wrong", "else q[k * M + r] = c;", "else q[r * K + k] = c;"),
+    ("group_start_not_advanced", "        start = end;\n    }", "    }"),
+    ("group_decreasing_end_kept", "if (end < start) end = start;", ""),
+    ("transpose_identity", "out[j * R + i] = in[i * C + j];", "out[i * C + j] = in[i * C + j];"),
+]
+
+
+@pytest.mark.parametrize("mid,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_mutant_is_caught(tmp_path, mid, old, new):
+    src = open(oracle.SOURCE).read()
+    assert src.count(old) == 1, f"mutation site for {mid} not found exactly once"
+    mutant_c = os.path.join(tmp_path, "mutant.c")
+    with open(mutant_c, "w") as f:
+        f.write(src.replace(old, new))
+    so = oracle.compile_source(mutant_c, os.path.join(tmp_path, "libmutant.so"))
+    failed = P.run_battery(oracle.Oracle(so))
+    assert failed, f"mutation {mid} was not caught by any pin"
