@@ -1,0 +1,129 @@
+// api.hip -- the C ABI of libmxq (declared in include/mxq.h): host-side argument
+// validation, then the kernel launches on the caller's stream.  No allocation,
+// no synchronisation, no state beyond a thread-local copy of the last HIP error.
+#include <hip/hip_runtime.h>
+
+#include "../../include/mxq.h"
+#include "internal.hpp"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Largest element count accepted by the flat kernels (keeps every index in range
+// of 64-bit arithmetic with a wide margin; 2^40 elements is 2 TB of bf16).
+constexpr int64_t kMaxElems = (int64_t)1 << 40;
+
+mxq_status check_2d(int64_t M, int64_t K)
+{
+    if (M < 0 || K < 0) return MXQ_ERR_SHAPE;
+    if (M > 0 && K > kMaxElems / M) return MXQ_ERR_SHAPE;
+    return MXQ_OK;
+}
+
+mxq_status hip_status(hipError_t e)
+{
+    if (e == hipSuccess) return MXQ_OK;
+    g_last_hip_error = (int)e;
+    return MXQ_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mxq_abi_version(void) { return MXQ_ABI_VERSION; }
+
+const char* mxq_status_string(int status)
+{
+    switch (status) {
+    case MXQ_OK: return "MXQ_OK";
+    case MXQ_ERR_NULL: return "MXQ_ERR_NULL: a required pointer is NULL";
+    case MXQ_ERR_SHAPE: return "MXQ_ERR_SHAPE: invalid size (negative, too large or not a required multiple)";
+    case MXQ_ERR_ALIGN: return "MXQ_ERR_ALIGN: a base pointer is not 16-byte aligned";
+    case MXQ_ERR_LAYOUT: return "MXQ_ERR_LAYOUT: unknown output layout";
+    case MXQ_ERR_WORKSPACE: return "MXQ_ERR_WORKSPACE: workspace missing or too small";
+    case MXQ_ERR_HIP: return "MXQ_ERR_HIP: a HIP runtime call failed";
+    case MXQ_ERR_NOT_IMPLEMENTED: return "MXQ_ERR_NOT_IMPLEMENTED";
+    default: return "unknown mxq_status";
+    }
+}
+
+int mxq_last_hip_error(void) { return g_last_hip_error; }
+
+mxq_status mxq_quantize_mx(const void* x_bf16, int64_t M, int64_t K, void* q_e4m3, void* s_e8m0, void* stream)
+{
+    mxq_status st = check_2d(M, K);
+    if (st != MXQ_OK) return st;
+    if (K % 32 != 0) return MXQ_ERR_SHAPE;
+    if (M == 0 || K == 0) return MXQ_OK;
+    if (!x_bf16 || !q_e4m3 || !s_e8m0) return MXQ_ERR_NULL;
+    if (!aligned16(x_bf16) || !aligned16(q_e4m3) || !aligned16(s_e8m0)) return MXQ_ERR_ALIGN;
+    return hip_status(mxq::launch_mx_quantize(x_bf16, M, K, q_e4m3, s_e8m0, (hipStream_t)stream));
+}
+
+mxq_status mxq_dequantize_mx(const void* q_e4m3, const void* s_e8m0, int64_t M, int64_t K, void* y_bf16,
+                             void* stream)
+{
+    mxq_status st = check_2d(M, K);
+    if (st != MXQ_OK) return st;
+    if (K % 32 != 0) return MXQ_ERR_SHAPE;
+    if (M == 0 || K == 0) return MXQ_OK;
+    if (!q_e4m3 || !s_e8m0 || !y_bf16) return MXQ_ERR_NULL;
+    if (!aligned16(q_e4m3) || !aligned16(s_e8m0) || !aligned16(y_bf16)) return MXQ_ERR_ALIGN;
+    return hip_status(mxq::launch_mx_dequantize(q_e4m3, s_e8m0, M, K, y_bf16, (hipStream_t)stream));
+}
+
+// Group scaling limits: rows fit the int32 offsets with room for chunk rounding;
+// K keeps every launch dimension in range.
+static const int64_t kGroupMaxRows = ((int64_t)1 << 31) - 1024;
+static const int64_t kGroupMaxK = (int64_t)1 << 23;
+static const int64_t kGroupMaxG = (int64_t)1 << 20;
+
+static mxq_status check_group_sizes(int64_t M, int64_t K, int64_t G)
+{
+    mxq_status st = check_2d(M, K);
+    if (st != MXQ_OK) return st;
+    if (M > kGroupMaxRows || K > kGroupMaxK || K % 8 != 0) return MXQ_ERR_SHAPE;
+    if (G < 1 || G > kGroupMaxG) return MXQ_ERR_SHAPE;
+    return MXQ_OK;
+}
+
+size_t mxq_group_scale_workspace_bytes(int64_t M, int64_t K, int32_t G)
+{
+    if (check_group_sizes(M, K, G) != MXQ_OK) return 0;
+    return mxq::group_scale_workspace_bytes(M, K, G);
+}
+
+mxq_status mxq_group_scale_fp8(const void* x_bf16, int64_t M, int64_t K, const int32_t* group_end_offs, int32_t G,
+                               int out_layout, void* q_e4m3, float* scales, void* workspace,
+                               size_t workspace_bytes, void* stream)
+{
+    mxq_status st = check_group_sizes(M, K, G);
+    if (st != MXQ_OK) return st;
+    if (out_layout != MXQ_LAYOUT_ROW && out_layout != MXQ_LAYOUT_COL) return MXQ_ERR_LAYOUT;
+    if (K == 0) return MXQ_OK;
+    if (!group_end_offs || !scales) return MXQ_ERR_NULL;
+    if (M > 0 && (!x_bf16 || !q_e4m3)) return MXQ_ERR_NULL;
+    if (!aligned16(scales) || (M > 0 && (!aligned16(x_bf16) || !aligned16(q_e4m3)))) return MXQ_ERR_ALIGN;
+    if (((uintptr_t)group_end_offs & 3u) != 0) return MXQ_ERR_ALIGN;
+    const size_t need = mxq::group_scale_workspace_bytes(M, K, G);
+    if (!workspace || workspace_bytes < need) return MXQ_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return MXQ_ERR_ALIGN;
+    return hip_status(mxq::launch_group_scale(x_bf16, (int)M, (int)K, group_end_offs, (int)G, out_layout,
+                                              q_e4m3, scales, workspace, (hipStream_t)stream));
+}
+
+mxq_status mxq_transpose_u8(const void* in, int64_t R, int64_t C, void* out, void* stream)
+{
+    mxq_status st = check_2d(R, C);
+    if (st != MXQ_OK) return st;
+    if (R == 0 || C == 0) return MXQ_OK;
+    if (!in || !out) return MXQ_ERR_NULL;
+    if (!aligned16(in) || !aligned16(out)) return MXQ_ERR_ALIGN;
+    return hip_status(mxq::launch_transpose_u8(in, R, C, out, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,199 @@
+// device_common.hpp -- small device helpers shared by the libmxq kernels (gfx950).
+//
+// Conversions used by the kernels (their rounding was checked exhaustively
+// against the reference encoder: every bf16 pattern x every E8M0 scale code for
+// quantization, every E4M3 code x every scale code for dequantization):
+//   v_cvt_scalef32_pk_fp8_bf16  bf16 pair / 2^e  -> E4M3 pair, nearest-even, no saturation
+//   v_cvt_pk_fp8_f32            fp32 pair        -> E4M3 pair, nearest-even, no saturation
+//   v_cvt_scalef32_pk_bf16_fp8  E4M3 pair * 2^e  -> bf16 pair, nearest-even, subnormals kept
+// "No saturation" means a magnitude that rounds past 448 becomes NaN, so every
+// quantizing path clamps to +-448 (times the block scale) before converting.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxq {
+
+typedef short v2i16 __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf16 __attribute__((ext_vector_type(2)));
+typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Streaming (non-temporal) 16- and 8-byte global accesses.
+__device__ __forceinline__ uint4 load_nt(const uint4* p)
+{
+    const u32x4 v = __builtin_nontemporal_load((const u32x4*)p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 load_nt(const uint2* p)
+{
+    const u32x2 v = __builtin_nontemporal_load((const u32x2*)p);
+    return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ void store_nt(uint4 v, uint4* p)
+{
+    const u32x4 w = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(w, (u32x4*)p);
+}
+__device__ __forceinline__ void store_nt(uint2 v, uint2* p)
+{
+    const u32x2 w = {v.x, v.y};
+    __builtin_nontemporal_store(w, (u32x2*)p);
+}
+
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b)
+{
+    v2u16 r = __builtin_elementwise_max(__builtin_bit_cast(v2u16, a), __builtin_bit_cast(v2u16, b));
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ uint32_t pk_min_u16(uint32_t a, uint32_t b)
+{
+    v2u16 r = __builtin_elementwise_min(__builtin_bit_cast(v2u16, a), __builtin_bit_cast(v2u16, b));
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// binary32 with the biased exponent e (1..254) and zero mantissa; e == 0 gives 2^-127.
+__device__ __forceinline__ float pow2_from_biased(uint32_t e)
+{
+    return __uint_as_float(e ? (e << 23) : 0x00400000u);
+}
+
+__device__ __forceinline__ float bf16_lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Max over each aligned quad of lanes (DPP quad permutations).
+__device__ __forceinline__ uint32_t quad_max_u32(uint32_t v)
+{
+    uint32_t t = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);  // [1,0,3,2]
+    v = v > t ? v : t;
+    t = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);           // [2,3,0,1]
+    return v > t ? v : t;
+}
+
+// Non-zero in each byte lane of the result whose input byte is 0x7F or 0xFF.
+__device__ __forceinline__ uint32_t nan_code_bytes(uint32_t q)
+{
+    uint32_t t = q & 0x7F7F7F7Fu;
+    return (t + 0x01010101u) & 0x80808080u;
+}
+
+// ------------------------------------------------------------------ scans --
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
+
+__device__ __forceinline__ int wave_incl_max(int v)
+{
+    const int lane = lane_id();
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        int t = __shfl_up(v, d, kWave);
+        if (lane >= d) v = v > t ? v : t;
+    }
+    return v;
+}
+
+__device__ __forceinline__ int wave_incl_sum(int v)
+{
+    const int lane = lane_id();
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        int t = __shfl_up(v, d, kWave);
+        if (lane >= d) v += t;
+    }
+    return v;
+}
+
+__device__ __forceinline__ int readlane(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
+
+// ------------------------------------------------------- token chunking ---
+//
+// Group g owns rows [end(g-1), end(g)) with end(g) = min(M, max(0, offs[0..g]))
+// (end(-1) = 0).  Pseudo-group G (when asked for) owns the rows past the last
+// end.  Every group is cut at the multiples of R, so a group [st, en) has
+// ceil(en/R) - floor(st/R) chunks (0 if empty), numbered consecutively over the
+// groups.  Aligned chunks keep full tiles aligned in both output layouts; the
+// total never exceeds ceil(M/R) + G.
+struct Chunk {
+    int g;    // group, G for the rows past the last end, -1 if the chunk id is unused
+    int r0;   // first row
+    int r1;   // one past the last row
+};
+
+// Executed by a whole wave (all 64 lanes active); the result is wave-uniform.
+template <int R>
+__device__ Chunk locate_chunk(const int32_t* __restrict__ offs, int G, int M, int j, bool with_tail)
+{
+    const int lane = lane_id();
+    const int ng = with_tail ? G + 1 : G;
+    int carry_end = 0, carry_cnt = 0;
+    for (int base = 0; base < ng; base += kWave) {
+        const int g = base + lane;
+        int e = (g < G) ? offs[g] : M;
+        e = e > 0 ? e : 0;
+        e = wave_incl_max(e);
+        e = e > carry_end ? e : carry_end;
+        e = e < M ? e : M;
+        int st = __shfl_up(e, 1, kWave);
+        if (lane == 0) st = carry_end;
+        const int cnt = (g < ng && e > st) ? ((e + R - 1) / R - st / R) : 0;
+        const int incl = wave_incl_sum(cnt) + carry_cnt;
+        const int excl = incl - cnt;
+        const unsigned long long hit = __ballot(cnt > 0 && j >= excl && j < incl);
+        if (hit) {
+            const int l = __builtin_ctzll(hit);
+            const int hst = readlane(st, l), hen = readlane(e, l), hexcl = readlane(excl, l);
+            const int i = j - hexcl;
+            const int a = (hst / R) * R;
+            Chunk c;
+            c.g = base + l;
+            c.r0 = hst > a + i * R ? hst : a + i * R;
+            c.r1 = hen < a + (i + 1) * R ? hen : a + (i + 1) * R;
+            return c;
+        }
+        carry_end = readlane(e, kWave - 1);
+        carry_cnt = readlane(incl, kWave - 1);
+    }
+    Chunk none;
+    none.g = -1;
+    none.r0 = 0;
+    none.r1 = 0;
+    return none;
+}
+
+// First chunk id and chunk count of group g (same numbering, no tail).
+template <int R>
+__device__ void group_chunk_span(const int32_t* __restrict__ offs, int G, int M, int gsel,
+                                 int* first, int* count)
+{
+    const int lane = lane_id();
+    int carry_end = 0, carry_cnt = 0;
+    for (int base = 0; base < G; base += kWave) {
+        const int g = base + lane;
+        int e = (g < G) ? offs[g] : M;
+        e = e > 0 ? e : 0;
+        e = wave_incl_max(e);
+        e = e > carry_end ? e : carry_end;
+        e = e < M ? e : M;
+        int st = __shfl_up(e, 1, kWave);
+        if (lane == 0) st = carry_end;
+        const int cnt = (g < G && e > st) ? ((e + R - 1) / R - st / R) : 0;
+        const int incl = wave_incl_sum(cnt) + carry_cnt;
+        if (gsel < base + kWave) {
+            const int l = gsel - base;
+            *count = readlane(cnt, l);
+            *first = readlane(incl, l) - *count;
+            return;
+        }
+        carry_end = readlane(e, kWave - 1);
+        carry_cnt = readlane(incl, kWave - 1);
+    }
+    *first = 0;
+    *count = 0;
+}
+
+}  // namespace mxq

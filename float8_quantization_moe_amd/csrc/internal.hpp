@@ -1,0 +1,20 @@
+// internal.hpp -- launchers shared between the kernel files and the C ABI layer.
+// Arguments reaching these functions have already been validated by api.hip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mxq {
+
+hipError_t launch_mx_quantize(const void* x, int64_t M, int64_t K, void* q, void* s, hipStream_t stream);
+hipError_t launch_mx_dequantize(const void* q, const void* s, int64_t M, int64_t K, void* y, hipStream_t stream);
+
+size_t group_scale_workspace_bytes(int64_t M, int64_t K, int32_t G);
+hipError_t launch_group_scale(const void* x, int M, int K, const int32_t* offs, int G, int layout,
+                              void* q, float* scales, void* workspace, hipStream_t stream);
+
+hipError_t launch_transpose_u8(const void* in, int64_t R, int64_t C, void* out, hipStream_t stream);
+
+}  // namespace mxq

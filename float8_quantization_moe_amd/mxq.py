@@ -1,0 +1,193 @@
+"""Python binding of libmxq (ctypes): argument marshalling only.
+
+Every function has the name of the C entry point it calls (see include/mxq.h)
+and takes torch tensors for the device buffers; torch is used for device memory
+and streams only.  All arithmetic runs in the HIP kernels of libmxq.so.  There
+is no fallback: if the library is missing or a call fails, an exception is
+raised.
+
+Sources of the operations: "[mxfp8 MoE training] Support mxfp8 all to all in
+expert parallel" (Summary) for the MXFP8 codec, and "[moe training] fix
+uncoalesced global accesses in per group rowwise scaling kernel" (Summary) for
+the group scaling and the layout transform.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmxq.so")
+
+MXQ_LAYOUT_ROW = 0
+MXQ_LAYOUT_COL = 1
+MXQ_OK = 0
+MXQ_ERR_NULL, MXQ_ERR_SHAPE, MXQ_ERR_ALIGN, MXQ_ERR_LAYOUT, MXQ_ERR_WORKSPACE, MXQ_ERR_HIP = 1, 2, 3, 4, 5, 6
+
+EXPORTED = ("mxq_abi_version", "mxq_status_string", "mxq_last_hip_error", "mxq_quantize_mx",
+            "mxq_dequantize_mx", "mxq_group_scale_workspace_bytes", "mxq_group_scale_fp8",
+            "mxq_transpose_u8")
+
+
+class MxqError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = lib().mxq_status_string(status).decode()
+        if status == MXQ_ERR_HIP:
+            msg += f" (hipError {lib().mxq_last_hip_error()})"
+        super().__init__(f"{where}: {msg}")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libmxq.so.  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"libmxq.so not found at {LIB_PATH}; build it with "
+                              "`python -m float8_quantization_moe_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        i32, i64, P, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
+        L.mxq_abi_version.restype = ctypes.c_int
+        L.mxq_abi_version.argtypes = []
+        L.mxq_status_string.restype = ctypes.c_char_p
+        L.mxq_status_string.argtypes = [ctypes.c_int]
+        L.mxq_last_hip_error.restype = ctypes.c_int
+        L.mxq_last_hip_error.argtypes = []
+        L.mxq_quantize_mx.restype = ctypes.c_int
+        L.mxq_quantize_mx.argtypes = [P, i64, i64, P, P, P]
+        L.mxq_dequantize_mx.restype = ctypes.c_int
+        L.mxq_dequantize_mx.argtypes = [P, P, i64, i64, P, P]
+        L.mxq_group_scale_workspace_bytes.restype = sz
+        L.mxq_group_scale_workspace_bytes.argtypes = [i64, i64, i32]
+        L.mxq_group_scale_fp8.restype = ctypes.c_int
+        L.mxq_group_scale_fp8.argtypes = [P, i64, i64, P, i32, ctypes.c_int, P, P, P, sz, P]
+        L.mxq_transpose_u8.restype = ctypes.c_int
+        L.mxq_transpose_u8.argtypes = [P, i64, i64, P, P]
+        _lib = L
+    return _lib
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None, numel=None) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} must hold {numel} elements, got {t.numel()}")
+    return t.data_ptr()
+
+
+def _check(status: int, where: str) -> None:
+    if status != MXQ_OK:
+        raise MxqError(status, where)
+
+
+def mxq_abi_version() -> int:
+    return lib().mxq_abi_version()
+
+
+def mxq_quantize_mx(x: torch.Tensor, q: torch.Tensor, s: torch.Tensor, stream=None) -> None:
+    """x (M, K) bf16 -> q (M, K) uint8 E4M3 codes, s (M, K/32) uint8 E8M0 codes."""
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D (M, K)")
+    M, K = x.shape
+    px = _dev(x, "x", torch.bfloat16)
+    pq = _dev(q, "q", torch.uint8, M * K)
+    ps = _dev(s, "s", torch.uint8, M * (K // 32) if K % 32 == 0 else None)
+    _check(lib().mxq_quantize_mx(px, M, K, pq, ps, _stream(stream)), "mxq_quantize_mx")
+
+
+def mxq_dequantize_mx(q: torch.Tensor, s: torch.Tensor, y: torch.Tensor, stream=None) -> None:
+    """q (M, K) uint8 E4M3 + s (M, K/32) uint8 E8M0 -> y (M, K) bf16."""
+    if y.dim() != 2:
+        raise ValueError("y must be 2-D (M, K)")
+    M, K = y.shape
+    pq = _dev(q, "q", torch.uint8, M * K)
+    ps = _dev(s, "s", torch.uint8, M * (K // 32) if K % 32 == 0 else None)
+    py = _dev(y, "y", torch.bfloat16)
+    _check(lib().mxq_dequantize_mx(pq, ps, M, K, py, _stream(stream)), "mxq_dequantize_mx")
+
+
+def mxq_group_scale_workspace_bytes(M: int, K: int, G: int) -> int:
+    return int(lib().mxq_group_scale_workspace_bytes(int(M), int(K), int(G)))
+
+
+def mxq_group_scale_fp8(x: torch.Tensor, group_end_offs: torch.Tensor, out_layout: int,
+                        q: torch.Tensor, scales: torch.Tensor, workspace: torch.Tensor,
+                        stream=None) -> None:
+    """x (M, K) bf16, group_end_offs int32[G] (device) -> q uint8 ((M, K) for ROW,
+    (K, M) for COL) and scales float32 (G, K)."""
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D (M, K)")
+    M, K = x.shape
+    G = group_end_offs.numel()
+    px = _dev(x, "x", torch.bfloat16)
+    po = _dev(group_end_offs, "group_end_offs", torch.int32)
+    pq = _dev(q, "q", torch.uint8, M * K)
+    ps = _dev(scales, "scales", torch.float32, G * K)
+    pw = _dev(workspace, "workspace")
+    wbytes = workspace.numel() * workspace.element_size()
+    _check(lib().mxq_group_scale_fp8(px, M, K, po, G, int(out_layout), pq, ps, pw, wbytes, _stream(stream)),
+           "mxq_group_scale_fp8")
+
+
+def mxq_transpose_u8(inp: torch.Tensor, out: torch.Tensor, stream=None) -> None:
+    """out (C, R) = inp (R, C)^T for uint8 tensors."""
+    if inp.dim() != 2:
+        raise ValueError("inp must be 2-D")
+    R, C = inp.shape
+    pi = _dev(inp, "inp", torch.uint8)
+    po = _dev(out, "out", torch.uint8, R * C)
+    _check(lib().mxq_transpose_u8(pi, R, C, po, _stream(stream)), "mxq_transpose_u8")
+
+
+# ---------------------------------------------------------------- helpers ---
+# Allocate outputs with torch and call the entry points above.
+
+def quantize_mx(x: torch.Tensor, stream=None):
+    M, K = x.shape
+    q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    s = torch.empty((M, K // 32), dtype=torch.uint8, device=x.device)
+    mxq_quantize_mx(x, q, s, stream)
+    return q, s
+
+
+def dequantize_mx(q: torch.Tensor, s: torch.Tensor, stream=None) -> torch.Tensor:
+    y = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    mxq_dequantize_mx(q, s, y, stream)
+    return y
+
+
+def group_scale_fp8(x: torch.Tensor, group_end_offs: torch.Tensor, out_layout: int = MXQ_LAYOUT_ROW,
+                    stream=None):
+    M, K = x.shape
+    G = group_end_offs.numel()
+    q = torch.empty((M, K) if out_layout == MXQ_LAYOUT_ROW else (K, M), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((G, K), dtype=torch.float32, device=x.device)
+    ws = torch.empty(max(mxq_group_scale_workspace_bytes(M, K, G), 16), dtype=torch.uint8, device=x.device)
+    mxq_group_scale_fp8(x, group_end_offs, out_layout, q, scales, ws, stream)
+    return q, scales
+
+
+def transpose_u8(inp: torch.Tensor, stream=None) -> torch.Tensor:
+    R, C = inp.shape
+    out = torch.empty((C, R), dtype=torch.uint8, device=inp.device)
+    mxq_transpose_u8(inp, out, stream)
+    return out

@@ -1,0 +1,177 @@
+/*
+ * mxq.h -- C ABI of libmxq: float8 quantization kernels for MoE token and expert
+ * buffers on AMD Instinct MI355X (gfx950).
+ *
+ * Sources:
+ *   "[mxfp8 MoE training] Support mxfp8 all to all in expert parallel"
+ *   (torchtitan PR 1765), Summary: the expert-parallel all-to-all payload is
+ *   quantized to mxfp8, the e4m3 data and the e8m0 scales travel in two
+ *   all_to_all_single calls, and the receiver dequantizes back to the original
+ *   precision.  mxq_quantize_mx / mxq_dequantize_mx are the two ends of that
+ *   exchange; the buffers they produce and consume are exactly the ones sent.
+ *
+ *   "[moe training] fix uncoalesced global accesses in per group rowwise scaling
+ *   kernel" (torchao PR 2761), Summary and Performance tables: a per-expert-group
+ *   float8 scaling kernel over a (tokens, hidden) bf16 tensor whose fp8 output
+ *   feeds the LHS of a scaled grouped GEMM, written either in one layout or in
+ *   the transposed one and then transformed.  mxq_group_scale_fp8 is that kernel
+ *   with both output layouts; mxq_transpose_u8 is the transform.
+ *
+ * Formats.  bf16 = bfloat16.  e4m3 = OCP FP8 E4M3 ("fn": bias 7, max 448, no
+ * infinity, S.1111.111 = NaN).  e8m0 = OCP E8M0 scale, value 2^(c-127), 0xFF =
+ * NaN.  MXFP8 = blocks of 32 consecutive elements along the last dimension
+ * sharing one e8m0 scale (OCP Microscaling v1.0).
+ *
+ * Conventions shared by every entry point:
+ *   - Pointers are DEVICE pointers (memory of the current HIP device), except
+ *     where a comment says otherwise.  Tensors are dense and row-major with no
+ *     padding between rows.  Base pointers must be 16-byte aligned
+ *     (MXQ_ERR_ALIGN otherwise); hipMalloc / torch allocations are.
+ *   - Ownership: the caller owns every buffer.  The library allocates nothing,
+ *     frees nothing, retains no pointer after the call returns and keeps no
+ *     state between calls; it is safe to call from several host threads.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Work is enqueued on it and the call returns without waiting.
+ *   - Argument errors are detected on the host, before anything is enqueued,
+ *     and returned as an mxq_status; the output buffers are then untouched.
+ *     A failed launch returns MXQ_ERR_HIP (see mxq_last_hip_error).  Faults
+ *     inside kernels surface, HIP-style, at the caller's next synchronisation.
+ *   - Results are bitwise deterministic: every reduction is a max.
+ */
+#ifndef MXQ_H
+#define MXQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MXQ_ABI_VERSION 1
+
+typedef enum mxq_status {
+    MXQ_OK = 0,
+    MXQ_ERR_NULL = 1,        /* a required pointer is NULL                          */
+    MXQ_ERR_SHAPE = 2,       /* a size is negative, too large, or not a multiple    */
+    MXQ_ERR_ALIGN = 3,       /* a base pointer is not 16-byte aligned               */
+    MXQ_ERR_LAYOUT = 4,      /* unknown mxq_layout value                            */
+    MXQ_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required          */
+    MXQ_ERR_HIP = 6,         /* a HIP runtime call failed (launch, device query)    */
+    MXQ_ERR_NOT_IMPLEMENTED = 7
+} mxq_status;
+
+typedef enum mxq_layout {
+    MXQ_LAYOUT_ROW = 0,      /* q[m*K + k]: same layout as X (K-contiguous)          */
+    MXQ_LAYOUT_COL = 1       /* q[k*M + m]: transposed (token-contiguous), i.e. the
+                                (K, M) row-major operand of a GEMM that contracts
+                                over the tokens of each group                        */
+} mxq_layout;
+
+/* MXQ_ABI_VERSION of the built library. */
+int mxq_abi_version(void);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* mxq_status_string(int status);
+
+/* hipError_t of the most recent MXQ_ERR_HIP returned on the calling thread
+ * (0 if none). */
+int mxq_last_hip_error(void);
+
+/*
+ * MXFP8 quantization of one all-to-all payload.
+ * Source: "[mxfp8 MoE training] Support mxfp8 all to all in expert parallel",
+ * Summary (quantize the inputs to mxfp8; e4m3 data; e8m0 scales).
+ *
+ *   x_bf16  (M, K) bf16 input, row-major.
+ *   q_e4m3  (M, K) uint8 output: e4m3 codes, row-major (the "e4m3 data" buffer).
+ *   s_e8m0  (M, K/32) uint8 output: e8m0 codes, row-major, unswizzled; scale b
+ *           of row m covers x[m, 32b .. 32b+31] (the "e8m0 scales" buffer).
+ *
+ * For each block: amax = max |x|; the scale code is floor(log2(amax)) - 8 + 127,
+ * clamped to [0, 254] (amax 0 or subnormal gives 0); each element is divided by
+ * the scale (exact) and rounded to the nearest e4m3 value, ties to even,
+ * saturating at +-448, sign kept (-0 -> 0x80).  A block containing Inf or NaN
+ * gets scale 0xFF and every code 0x7F.
+ *
+ * Requires K % 32 == 0 (MXQ_ERR_SHAPE), M >= 0, K >= 0, M*K < 2^62.
+ * M == 0 or K == 0 is a no-op that returns MXQ_OK.  A token-row split of Q and S
+ * (the all-to-all's input splits) keeps every block whole.
+ */
+mxq_status mxq_quantize_mx(const void* x_bf16, int64_t M, int64_t K,
+                           void* q_e4m3, void* s_e8m0, void* stream);
+
+/*
+ * MXFP8 dequantization of one received payload back to bf16.
+ * Source: "[mxfp8 MoE training] Support mxfp8 all to all in expert parallel",
+ * Summary (dequantize outputs back to original precision).
+ *
+ *   q_e4m3  (M, K) uint8 e4m3 codes; s_e8m0 (M, K/32) uint8 e8m0 codes, both as
+ *           produced by mxq_quantize_mx (or received from a peer).
+ *   y_bf16  (M, K) bf16 output, row-major.
+ *
+ * y = e4m3(q) * 2^(s-127) rounded once to bf16 (nearest, ties to even,
+ * subnormals kept, overflow to +-Inf).  For s >= 3 the product is exact.
+ * A NaN code (0x7F, 0xFF) or scale 0xFF gives bf16 NaN 0x7FC0.
+ * Requires K % 32 == 0; M == 0 or K == 0 is a no-op.
+ */
+mxq_status mxq_dequantize_mx(const void* q_e4m3, const void* s_e8m0, int64_t M, int64_t K,
+                             void* y_bf16, void* stream);
+
+/*
+ * Bytes of device workspace mxq_group_scale_fp8 needs for these sizes (0 for
+ * invalid sizes).  The workspace holds per-chunk partial maxima; its contents
+ * need no initialisation and are meaningless after the call.
+ */
+size_t mxq_group_scale_workspace_bytes(int64_t M, int64_t K, int32_t G);
+
+/*
+ * Per-expert-group float8 scaling of a token tensor.
+ * Source: "[moe training] fix uncoalesced global accesses in per group rowwise
+ * scaling kernel", Summary (per-group scaling whose output is the LHS operand of
+ * the scaled grouped GEMM; row-major or column-major output).
+ *
+ *   x_bf16          (M, K) bf16 tokens, row-major; the tokens of group g are the
+ *                   rows [end[g-1], end[g]) (end[-1] = 0).
+ *   group_end_offs  DEVICE int32[G]: cumulative end offsets, non-decreasing,
+ *                   end[G-1] == M by contract.  They are read only on the device
+ *                   (no device-to-host copy, no host synchronisation).  Offsets
+ *                   outside the contract are clamped, not trapped: end[g] is
+ *                   taken as min(M, max(end[0..g], 0)); rows at or past the
+ *                   last clamped end belong to no group and get code 0x00.
+ *   G               number of groups, >= 1; empty groups are allowed.
+ *   out_layout      MXQ_LAYOUT_ROW: q is (M, K); MXQ_LAYOUT_COL: q is (K, M).
+ *   q_e4m3          uint8 e4m3 output in out_layout.
+ *   scales          DEVICE float[G*K] output, (G, K) row-major: the multiplier s
+ *                   applied before the cast (dequantize as e4m3(q) / s).
+ *   workspace       DEVICE scratch of at least
+ *                   mxq_group_scale_workspace_bytes(M, K, G) bytes, 16-B aligned.
+ *
+ * For each group g and column k: amax = max |x[r,k]| over the group's rows;
+ * s = 448 / max(amax, 1e-12) in binary32 (correctly rounded); q = e4m3 of the
+ * binary32 product x*s, nearest, ties to even, saturating at +-448.  An empty
+ * group has amax 0.  A column holding Inf or NaN gets s = NaN and q = 0x7F.
+ *
+ * Requires K % 8 == 0, 0 <= M < 2^31, K < 2^31 (MXQ_ERR_SHAPE), G >= 1.  K == 0
+ * is a no-op; M == 0 still writes the (G, K) scales.
+ */
+mxq_status mxq_group_scale_fp8(const void* x_bf16, int64_t M, int64_t K,
+                               const int32_t* group_end_offs, int32_t G, int out_layout,
+                               void* q_e4m3, float* scales,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Byte transpose: out (C, R) = in (R, C)^T, both row-major.  The layout
+ * transform between the two outputs of mxq_group_scale_fp8.
+ * Source: "[moe training] fix uncoalesced global accesses in per group rowwise
+ * scaling kernel", Summary (write one layout, then transform to the other).
+ * Any R, C >= 0 (R*C < 2^62); R == 0 or C == 0 is a no-op; in and out must not
+ * overlap.
+ */
+mxq_status mxq_transpose_u8(const void* in, int64_t R, int64_t C, void* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXQ_H */

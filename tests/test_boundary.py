@@ -1,0 +1,128 @@
+"""The C-ABI library without a GPU: it loads, exports every entry point the
+header declares, and rejects bad arguments on the host before touching a device
+(no kernel is ever launched here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxq.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mxq_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    from float8_quantization_moe_amd import mxq
+    if not os.path.exists(mxq.LIB_PATH):
+        pytest.fail("libmxq.so is not built (run `python -m float8_quantization_moe_amd.build`)")
+    return mxq.lib()
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for n in ("mxq_quantize_mx", "mxq_dequantize_mx", "mxq_group_scale_fp8",
+              "mxq_group_scale_workspace_bytes", "mxq_transpose_u8", "mxq_abi_version"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(L):
+    from float8_quantization_moe_amd import mxq
+    raw = ctypes.CDLL(mxq.LIB_PATH)
+    for name in _declared():
+        assert hasattr(raw, name), f"{name} is declared in mxq.h but not exported"
+    assert sorted(mxq.EXPORTED) == _declared()
+
+
+def test_abi_version_and_status_strings(L):
+    assert L.mxq_abi_version() == 1
+    for code in range(0, 8):
+        assert L.mxq_status_string(code).startswith(b"MXQ_")
+    assert L.mxq_status_string(99) == b"unknown mxq_status"
+    assert L.mxq_last_hip_error() == 0
+
+
+A = 1 << 20   # a fake, 16-byte aligned "device" address.  Every call below either fails
+              # validation or is a no-op, so nothing is ever enqueued with it.
+
+
+def test_quantize_mx_argument_errors(L):
+    S = 0
+    assert L.mxq_quantize_mx(A, 4, 31, A, A, S) == 2          # K % 32
+    assert L.mxq_quantize_mx(A, -1, 32, A, A, S) == 2         # negative
+    assert L.mxq_quantize_mx(A, 1 << 30, 1 << 30, A, A, S) == 2  # too large
+    assert L.mxq_quantize_mx(0, 4, 32, A, A, S) == 1          # null
+    assert L.mxq_quantize_mx(A, 4, 32, 0, A, S) == 1
+    assert L.mxq_quantize_mx(A, 4, 32, A, 0, S) == 1
+    assert L.mxq_quantize_mx(A + 8, 4, 32, A, A, S) == 3      # misaligned
+    assert L.mxq_quantize_mx(A, 4, 32, A + 1, A, S) == 3
+    assert L.mxq_quantize_mx(0, 0, 32, 0, 0, S) == 0          # empty: no-op
+    assert L.mxq_quantize_mx(0, 7, 0, 0, 0, S) == 0
+
+
+def test_dequantize_mx_argument_errors(L):
+    S = 0
+    assert L.mxq_dequantize_mx(A, A, 4, 48, A, S) == 2
+    assert L.mxq_dequantize_mx(0, A, 4, 32, A, S) == 1
+    assert L.mxq_dequantize_mx(A, 0, 4, 32, A, S) == 1
+    assert L.mxq_dequantize_mx(A, A, 4, 32, 0, S) == 1
+    assert L.mxq_dequantize_mx(A, A + 4, 4, 32, A, S) == 3
+    assert L.mxq_dequantize_mx(0, 0, 0, 64, 0, S) == 0
+
+
+def test_group_scale_argument_errors(L):
+    S = 0
+    ws = L.mxq_group_scale_workspace_bytes(512, 256, 4)
+    assert ws > 0 and ws % 256 == 0
+    assert L.mxq_group_scale_workspace_bytes(512, 250, 4) == 0   # K % 8
+    assert L.mxq_group_scale_workspace_bytes(512, 256, 0) == 0   # G < 1
+    assert L.mxq_group_scale_workspace_bytes(-1, 256, 4) == 0
+    f = L.mxq_group_scale_fp8
+    assert f(A, 512, 252, A, 4, 0, A, A, A, ws, S) == 2           # K % 8
+    assert f(A, 512, 256, A, 0, 0, A, A, A, ws, S) == 2           # G < 1
+    assert f(A, 1 << 31, 256, A, 4, 0, A, A, A, ws, S) == 2       # rows beyond int32 offsets
+    assert f(A, 512, 256, A, 4, 2, A, A, A, ws, S) == 4           # layout
+    assert f(A, 512, 256, A, 4, -1, A, A, A, ws, S) == 4
+    assert f(0, 512, 256, A, 4, 0, A, A, A, ws, S) == 1           # null x
+    assert f(A, 512, 256, 0, 4, 0, A, A, A, ws, S) == 1           # null offsets
+    assert f(A, 512, 256, A, 4, 0, 0, A, A, ws, S) == 1           # null q
+    assert f(A, 512, 256, A, 4, 0, A, 0, A, ws, S) == 1           # null scales
+    assert f(A, 512, 256, A, 4, 0, A, A, 0, ws, S) == 5           # no workspace
+    assert f(A, 512, 256, A, 4, 0, A, A, A, ws - 1, S) == 5       # workspace too small
+    assert f(A + 2, 512, 256, A, 4, 0, A, A, A, ws, S) == 3       # misaligned x
+    assert f(A, 512, 256, A + 2, 4, 0, A, A, A, ws, S) == 3       # misaligned offsets
+    assert f(A, 512, 256, A, 4, 0, A, A + 4, A, ws, S) == 3       # misaligned scales
+    assert f(A, 512, 0, A, 4, 0, A, A, A, ws, S) == 0             # K == 0: no-op
+
+
+def test_transpose_argument_errors(L):
+    S = 0
+    assert L.mxq_transpose_u8(A, -3, 4, A, S) == 2
+    assert L.mxq_transpose_u8(0, 3, 4, A, S) == 1
+    assert L.mxq_transpose_u8(A, 3, 4, 0, S) == 1
+    assert L.mxq_transpose_u8(A + 1, 3, 4, A, S) == 3
+    assert L.mxq_transpose_u8(0, 0, 4, 0, S) == 0
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    from float8_quantization_moe_amd import mxq
+    x = torch.zeros((4, 32), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        mxq.mxq_quantize_mx(x, torch.zeros(128, dtype=torch.uint8), torch.zeros(4, dtype=torch.uint8))
+
+
+def test_product_path_does_not_import_the_oracle():
+    """The HIP binding and package never reference the oracle."""
+    pkg = os.path.join(ROOT, "float8_quantization_moe_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, fn)).read()
+                assert "oracle" not in text.lower(), f"{fn} mentions the oracle"

@@ -1,0 +1,181 @@
+"""Per-expert-group float8 scaling and the byte transpose on the GPU, bit-exact
+against the CPU oracle (codes byte for byte, scales bit for bit).
+
+"[moe training] fix uncoalesced global accesses in per group rowwise scaling
+kernel", Summary and Performance: per-group scaling of a (16640, 5120) bf16
+token tensor for 16 to 128 expert groups, row-major or column-major output,
+and the transform between the two.
+"""
+import numpy as np
+import pytest
+import torch
+
+import _golden
+import gpu_util as U
+import oracle
+import workloads as W
+from float8_quantization_moe_amd import mxq
+
+pytestmark = pytest.mark.gpu
+
+ROW, COL = mxq.MXQ_LAYOUT_ROW, mxq.MXQ_LAYOUT_COL
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "these tests need an MI355X"
+    mxq.lib()
+    yield
+
+
+def run_group(x_bits, ends, layout, x_dev=None):
+    M, K = x_bits.shape
+    G = len(ends)
+    x = U.dev_bf16(x_bits) if x_dev is None else x_dev
+    offs = torch.tensor(np.asarray(ends, np.int32), device="cuda")
+    qg = U.Guarded(M * K, torch.uint8, (M, K) if layout == ROW else (K, M))
+    sg = U.Guarded(G * K, torch.float32, (G, K))
+    ws = torch.empty(max(16, mxq.mxq_group_scale_workspace_bytes(M, K, G)), dtype=torch.uint8, device="cuda")
+    ws.fill_(0xAB)    # the workspace needs no initialisation
+    mxq.mxq_group_scale_fp8(x, offs, layout, qg.t, sg.t, ws)
+    torch.cuda.synchronize()
+    assert qg.guard_intact() and sg.guard_intact(), "wrote past the end"
+    return U.host_u8(qg.t), U.host_f32_bits(sg.t)
+
+
+def check_group(x_bits, ends, layouts=(ROW, COL), name=""):
+    want_q, want_s = U.oracle_group_scale_row(x_bits, ends)
+    want_s = want_s.view(np.uint32)
+    x = U.dev_bf16(x_bits)
+    out = {}
+    for layout in layouts:
+        q, s = run_group(x_bits, ends, layout, x)
+        assert np.array_equal(s, want_s), f"{name} layout {layout} scales: {U.first_mismatch(s, want_s)}"
+        qr = q if layout == ROW else q.T
+        assert np.array_equal(qr, want_q), f"{name} layout {layout} codes: {U.first_mismatch(qr, want_q)}"
+        out[layout] = q
+    return out
+
+
+def test_tiny_four_groups():
+    """(512, 256), group sizes 100, 37, 0, 375 (an empty group)."""
+    check_group(W.bf16_bits(W.tiny_x(0)), W.tiny_group_ends(), name="tiny")
+
+
+def test_hand_worked_cases_on_device():
+    for c in _golden.load_group_cases():
+        x = np.zeros((c["M"], 8), np.uint16)
+        x[:, :c["K"]] = np.array(c["x"], np.uint16)
+        for layout in (ROW, COL):
+            q, s = run_group(x, c["ends"], layout)
+            qr = q if layout == ROW else q.T
+            assert np.array_equal(qr[:, :c["K"]], np.array(c["q"], np.uint8)), (c["name"], layout)
+            assert np.array_equal(s[:, :c["K"]], np.array(c["scales"], np.uint32)), (c["name"], layout)
+
+
+def _sizes_to_ends(sizes):
+    return np.cumsum(sizes).astype(np.int32)
+
+
+EDGE_CASES = {
+    "one_group": (300, 64, [300]),
+    "empty_first_middle_last": (400, 72, [0, 150, 0, 0, 250, 0]),
+    "one_row_groups": (130, 40, [1] * 70 + [60]),
+    "ragged_rows_not_mult_16": (333, 136, [100, 33, 200]),
+    "rows_not_mult_128": (1000, 520, [129, 127, 1, 255, 488]),
+    "k_partial_strip": (256, 264, [128, 128]),
+    "k_eight": (200, 8, [50, 150]),
+    "many_groups": (5000, 128, None),          # 300 Zipf groups: several 64-group scan batches
+    "groups_mostly_empty": (640, 64, [0] * 500 + [640] + [0] * 499),
+}
+
+
+@pytest.mark.parametrize("case", list(EDGE_CASES), ids=list(EDGE_CASES))
+def test_edge_cases(case):
+    M, K, sizes = EDGE_CASES[case]
+    rng = np.random.default_rng(len(case) * 1000 + M)
+    if sizes is None:
+        ends = W.zipf_group_ends(M, 300, seed=4)
+    else:
+        ends = _sizes_to_ends(sizes)
+    x = (rng.standard_normal((M, K)) * np.exp(rng.standard_normal((M, 1)))).astype(np.float32)
+    x_bits = (x.view(np.uint32) >> 16).astype(np.uint16)
+    check_group(x_bits, ends, name=case)
+
+
+def test_out_of_contract_offsets_are_clamped():
+    M, K = 300, 64
+    rng = np.random.default_rng(21)
+    x_bits = (rng.standard_normal((M, K)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    for ends in ([100, 50, 400], [-5, 120, 250], [64, 64, 64], [0]):
+        check_group(x_bits, np.array(ends, np.int32), name=f"ends {ends}")
+
+
+def test_nonfinite_columns():
+    M, K = 260, 48
+    rng = np.random.default_rng(22)
+    x_bits = (rng.standard_normal((M, K)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    x_bits[5, 3] = 0x7F80      # +Inf in group 0, column 3
+    x_bits[200, 17] = 0xFFC0   # NaN in group 1, column 17
+    x_bits[120, 40] = 0xFF80   # -Inf in group 1
+    check_group(x_bits, _sizes_to_ends([100, 160]), name="nonfinite")
+
+
+def test_zero_rows_writes_scales_only():
+    K, G = 64, 3
+    x = torch.empty((0, K), dtype=torch.bfloat16, device="cuda")
+    offs = torch.zeros(G, dtype=torch.int32, device="cuda")
+    q = torch.empty((0, K), dtype=torch.uint8, device="cuda")
+    scales = torch.zeros((G, K), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(16, mxq.mxq_group_scale_workspace_bytes(0, K, G)), dtype=torch.uint8, device="cuda")
+    mxq.mxq_group_scale_fp8(x, offs, ROW, q, scales, ws)
+    torch.cuda.synchronize()
+    _, want = oracle.group_scale(np.zeros((0, K), np.uint16), [0] * G)
+    assert np.array_equal(U.host_f32_bits(scales), want.view(np.uint32))
+
+
+@pytest.fixture(scope="module")
+def tokens_bits():
+    return W.bf16_bits(W.moe_tokens())
+
+
+def test_tokens_g16_row_full_size(tokens_bits):
+    """(16640, 5120), 16 Zipf(1.1) groups, row-major output: every byte."""
+    ends = W.zipf_group_ends(W.TOKENS_SHAPE[0], 16)
+    check_group(tokens_bits, ends, layouts=(ROW,), name="G=16")
+
+
+@pytest.mark.parametrize("G", [32, 64, 128])
+def test_tokens_both_layouts_and_transforms(tokens_bits, G):
+    """(16640, 5120) with 32/64/128 groups: both layouts bit-exact, and each
+    transformed into the other on the device equals the other."""
+    ends = W.zipf_group_ends(W.TOKENS_SHAPE[0], G)
+    out = check_group(tokens_bits, ends, name=f"G={G}")
+    row = torch.from_numpy(out[ROW]).cuda()
+    col = torch.from_numpy(out[COL]).cuda()
+    col_to_row = mxq.transpose_u8(col)
+    row_to_col = mxq.transpose_u8(row)
+    torch.cuda.synchronize()
+    assert torch.equal(col_to_row, row) and torch.equal(row_to_col, col)
+
+
+def test_group_scaling_is_deterministic(tokens_bits):
+    ends = W.zipf_group_ends(W.TOKENS_SHAPE[0], 64)
+    x = U.dev_bf16(tokens_bits[:4096])
+    ends = np.minimum(ends, 4096).astype(np.int32)
+    a = run_group(tokens_bits[:4096], ends, COL, x)
+    b = run_group(tokens_bits[:4096], ends, COL, x)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("R,C", [(1, 1), (3, 7), (16, 16), (128, 128), (129, 257), (1000, 48), (5120, 16640),
+                                 (64, 1000), (17, 4096)])
+def test_transpose_shapes(R, C):
+    rng = np.random.default_rng(R * 31 + C)
+    a = rng.integers(0, 256, (R, C)).astype(np.uint8)
+    og = U.Guarded(R * C, torch.uint8, (C, R))
+    mxq.mxq_transpose_u8(torch.from_numpy(a).cuda(), og.t)
+    torch.cuda.synchronize()
+    got = U.host_u8(og.t)
+    assert np.array_equal(got, a.T), U.first_mismatch(got, a.T)
+    assert og.guard_intact()
