@@ -1,0 +1,369 @@
+#!/usr/bin/env python3
+"""Benchmark of the float8 MoE quantization hot path on one MI355X (gfx950).
+
+One step is one pass of the whole path over one batch of synthetic MoE-shaped
+input, every kernel from libmxq:
+  1. mxq_quantize_mx    dispatch payload X (65536, 5120) bf16 -> e4m3 (65536, 5120)
+                        + e8m0 (65536, 160): the two all-to-all send buffers
+  2. mxq_dequantize_mx  those two buffers -> bf16 (65536, 5120)
+  3. mxq_group_scale_fp8  tokens (16640, 5120) bf16, 16 Zipf(1.1) expert groups,
+                        row-major e4m3 + (16, 5120) fp32 scales
+  4. mxq_group_scale_fp8  the same token shape, 128 groups, column-major e4m3
+  5. mxq_transpose_u8   that column-major output -> row-major
+Sources: "[mxfp8 MoE training] Support mxfp8 all to all in expert parallel"
+(Summary; Performance: seq 8192 x local batch 8 tokens, dim 5120, 16 experts)
+and "[moe training] fix uncoalesced global accesses in per group rowwise scaling
+kernel" (Summary; Performance tables at (16640, 5120), 16..128 groups).
+
+The metric is achieved HBM bandwidth: algorithmic bytes (each input read once,
+each output written once) over time.  Inputs are resident in device memory
+before timing starts; several independent buffer sets are rotated so that no
+step finds the previous step's data in the 256 MB last-level cache.
+
+Prints ONE JSON line (see the keys below).  --gpus N > 1 is refused: this path
+runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+METRIC = "achieved HBM GB/s (and % of peak) for MXFP8 quant+dequant and group scaling"
+HBM_PEAK_GBPS = 8000.0                     # MI355X HBM3E, 8 TB/s
+DISPATCH = (65536, 5120)
+TOKENS = (16640, 5120)
+G_ROW, G_COL = 16, 128
+PROFILES = os.path.join(HERE, "profiles")
+TRAFFIC_FILE = os.path.join(PROFILES, "traffic_counters.json")
+
+
+def mx_bytes(M, K):                # read bf16, write e4m3 + e8m0 (or the reverse)
+    return M * K * 2 + M * K + M * K // 32
+
+
+def group_bytes(M, K, G):          # read bf16, write e4m3 + fp32 (G, K) scales
+    return M * K * 3 + 4 * G * K
+
+
+def transpose_bytes(M, K):         # read and write one byte per element
+    return 2 * M * K
+
+
+def kernel_source_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(HERE, "float8_quantization_moe_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--rotate", type=int, default=4, help="independent buffer sets cycled through")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-mx-rows", type=int, default=16384, help="dispatch rows in the CPU sample")
+    p.add_argument("--cpu-group-rows", type=int, default=8320, help="token rows in the CPU sample")
+    p.add_argument("--ingest-counters", nargs=3, metavar=("STATS_CSV", "FETCH_CSV", "WRITE_CSV"),
+                   help="turn rocprofv3 outputs of this script (kernel stats, FETCH_SIZE and WRITE_SIZE "
+                        "counter collections) into the summaries under profiles/ and exit")
+    p.add_argument("--profile-commands", default="", help="text recorded with --ingest-counters")
+    return p.parse_args()
+
+
+COUNTER_SOURCES = ["mx_codec.hip", "device_common.hpp"]
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+COPY_BYTES = 1 << 30       # the 1 GiB device copies of the streaming-ceiling leg
+
+
+def ingest_counters(stats_csv, fetch_csv, write_csv, commands):
+    """Summaries for profiles/: per-kernel durations (kernel-trace stats) and
+    HBM bytes per dispatch from FETCH_SIZE / WRITE_SIZE (KiB), each scaled by what
+    the counter reads for the 1 GiB copies of known size."""
+    import csv
+    import collections
+    import statistics
+
+    def per_kernel(path, field="Counter_Value"):
+        agg = collections.defaultdict(list)
+        for r in csv.DictReader(open(path)):
+            agg[r["Kernel_Name"].split("(")[0]].append(float(r[field]))
+        return agg
+
+    fetch, write = per_kernel(fetch_csv), per_kernel(write_csv)
+    f_copy = max(fetch[COPY_KERNEL]) * 1024.0
+    w_copy = max(write[COPY_KERNEL]) * 1024.0
+    f_scale, w_scale = COPY_BYTES / f_copy, COPY_BYTES / w_copy
+    stats = {r["Name"].split("(")[0]: r for r in csv.DictReader(open(stats_csv))}
+    algo = {"mxq::mx_quantize_kernel": mx_bytes(*DISPATCH), "mxq::mx_dequantize_kernel": mx_bytes(*DISPATCH)}
+    lines = ["# HBM traffic per dispatch, hot-path step (dispatch payload 65536x5120, tokens 16640x5120)", "",
+             "Commands (from the repository root):", "", "```", commands.strip(), "```", "",
+             f"Calibration: {COPY_KERNEL} copies of 1 GiB read {f_copy / 1024:.1f} KiB by FETCH_SIZE and "
+             f"write {w_copy / 1024:.1f} KiB by WRITE_SIZE; scale factors {f_scale:.4f} (fetch) and "
+             f"{w_scale:.4f} (write).", "",
+             "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled HBM bytes / dispatch | "
+             "algorithmic bytes | ratio |", "|---|---|---|---|---|---|---|"]
+    out = {"source_files": COUNTER_SOURCES, "fetch_scale": f_scale, "write_scale": w_scale, "kernels": {}}
+    src_hash = kernel_source_hash(COUNTER_SOURCES)
+    for k in sorted(fetch):
+        if k == COPY_KERNEL or k not in write:
+            continue
+        fk, wk = statistics.mean(fetch[k]), statistics.mean(write[k])
+        hbm = fk * 1024 * f_scale + wk * 1024 * w_scale
+        a = algo.get(k)
+        lines.append(f"| {k} | {len(fetch[k])} | {fk:.1f} | {wk:.1f} | {hbm:,.0f} | "
+                     f"{a if a else '-'} | {hbm / a if a else float('nan'):.4f} |")
+        if a:
+            out["kernels"][k.split("::")[-1]] = {"hbm_bytes_per_launch": round(hbm), "algorithmic_bytes": a,
+                                                 "source_sha256": src_hash}
+    lines += ["", "Kernel durations (rocprofv3 --kernel-trace --stats):", "",
+              "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
+    for k, r in stats.items():
+        lines.append(f"| {k} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
+                     f"{float(r['MaxNs']) / 1e3:.2f} |")
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(os.path.join(PROFILES, "hbm_traffic_hot_path_step.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print("\n".join(lines))
+
+
+def cpu_info():
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count()
+    return model, n
+
+
+def main():
+    args = parse_args()
+    if args.ingest_counters:
+        ingest_counters(*args.ingest_counters, args.profile_commands)
+        return
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} (WORLD_SIZE={world}) is not "
+              "supported.  The quantization kernels shard by token rows with no exchange of their own; "
+              "see the design notes for how the all-to-all would carry the buffers.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import workloads as W
+    from float8_quantization_moe_amd import mxq
+
+    assert torch.cuda.is_available(), "bench.py needs an MI355X"
+    mxq.lib()                                     # fails loudly if libmxq.so is missing
+    dev = torch.device("cuda:0")
+    ROW, COL = mxq.MXQ_LAYOUT_ROW, mxq.MXQ_LAYOUT_COL
+
+    # ------------------------------------------------------ synthetic inputs --
+    M1, K1 = DISPATCH
+    M2, K2 = TOKENS
+    x1_host = W.dispatch_payload(M1, K1, seed=0)
+    x2_host = W.moe_tokens(M2, K2, seed=0)
+    ends16 = W.zipf_group_ends(M2, G_ROW, seed=1)
+    ends128 = W.zipf_group_ends(M2, G_COL, seed=1)
+    x1_dev = x1_host.to(dev)
+    x2_dev = x2_host.to(dev)
+    offs16 = torch.from_numpy(ends16).to(dev)
+    offs128 = torch.from_numpy(ends128).to(dev)
+
+    class BufferSet:
+        def __init__(self):
+            self.x1 = x1_dev.clone()
+            self.q1 = torch.empty((M1, K1), dtype=torch.uint8, device=dev)
+            self.s1 = torch.empty((M1, K1 // 32), dtype=torch.uint8, device=dev)
+            self.y1 = torch.empty((M1, K1), dtype=torch.bfloat16, device=dev)
+            self.x2 = x2_dev.clone()
+            self.x3 = x2_dev.clone()              # the 128-group pass reads its own copy
+            self.q2 = torch.empty((M2, K2), dtype=torch.uint8, device=dev)
+            self.sc2 = torch.empty((G_ROW, K2), dtype=torch.float32, device=dev)
+            self.q3 = torch.empty((K2, M2), dtype=torch.uint8, device=dev)
+            self.sc3 = torch.empty((G_COL, K2), dtype=torch.float32, device=dev)
+            self.q3t = torch.empty((M2, K2), dtype=torch.uint8, device=dev)
+
+    sets = [BufferSet() for _ in range(max(1, args.rotate))]
+    ws = torch.empty(max(mxq.mxq_group_scale_workspace_bytes(M2, K2, G_ROW),
+                         mxq.mxq_group_scale_workspace_bytes(M2, K2, G_COL)), dtype=torch.uint8, device=dev)
+    del x1_dev, x2_dev
+    torch.cuda.synchronize()
+
+    calls = ["mx_quantize", "mx_dequantize", "group_scale_g16_row", "group_scale_g128_col", "transpose_col_to_row"]
+    call_bytes = {
+        "mx_quantize": mx_bytes(M1, K1),
+        "mx_dequantize": mx_bytes(M1, K1),
+        "group_scale_g16_row": group_bytes(M2, K2, G_ROW),
+        "group_scale_g128_col": group_bytes(M2, K2, G_COL),
+        "transpose_col_to_row": transpose_bytes(M2, K2),
+    }
+    step_bytes = sum(call_bytes.values())
+    stream = torch.cuda.current_stream()
+
+    def step(i, events=None):
+        b = sets[i % len(sets)]
+        fns = [
+            lambda: mxq.mxq_quantize_mx(b.x1, b.q1, b.s1, stream),
+            lambda: mxq.mxq_dequantize_mx(b.q1, b.s1, b.y1, stream),
+            lambda: mxq.mxq_group_scale_fp8(b.x2, offs16, ROW, b.q2, b.sc2, ws, stream),
+            lambda: mxq.mxq_group_scale_fp8(b.x3, offs128, COL, b.q3, b.sc3, ws, stream),
+            lambda: mxq.mxq_transpose_u8(b.q3, b.q3t, stream),
+        ]
+        for j, fn in enumerate(fns):
+            if events is not None:
+                events[j][0].record(stream)
+            fn()
+            if events is not None:
+                events[j][1].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # ------------------------------------------------------------ timed run --
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in calls]
+          for _ in range(args.steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    h0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i, ev[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    h1 = time.perf_counter()
+    host_ms = (h1 - h0) * 1e3 / args.steps
+    dev_ms = t_start.elapsed_time(t_end) / args.steps
+    ms_per_step = max(host_ms, dev_ms)
+    per_call_us = {c: 1e3 * float(np.mean([ev[i][j][0].elapsed_time(ev[i][j][1]) for i in range(args.steps)]))
+                   for j, c in enumerate(calls)}
+    kernels = {c: {"avg_us": round(per_call_us[c], 2), "algorithmic_bytes": call_bytes[c],
+                   "GBps": round(call_bytes[c] / (per_call_us[c] * 1e3), 1),
+                   "frac_of_peak": round(call_bytes[c] / (per_call_us[c] * 1e3) / HBM_PEAK_GBPS, 4)}
+               for c in calls}
+    value = step_bytes / (ms_per_step * 1e6)          # GB/s
+
+    # streaming ceiling for context: a device-to-device copy of 1 GiB
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(10):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = 2 * (1 << 30) * 10 / (e0.elapsed_time(e1) * 1e6)
+    del src, dst
+
+    # --------------------------------------------------- dominant kernel ---
+    # the single-kernel call that takes the longest; its launch is bracketed by
+    # events on the stream it runs on
+    dom = max(("mx_quantize", "mx_dequantize"), key=lambda c: per_call_us[c])
+    dom_kernel = {"mx_quantize": "mx_quantize_kernel", "mx_dequantize": "mx_dequantize_kernel"}[dom]
+    achieved = call_bytes[dom] / (per_call_us[dom] * 1e3)
+    traffic = None
+    traffic_note = "no counter file"
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        entry = tr.get("kernels", {}).get(dom_kernel)
+        if entry and entry.get("source_sha256") == kernel_source_hash(COUNTER_SOURCES):
+            traffic = int(entry["hbm_bytes_per_launch"])
+            traffic_note = "rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated"
+        elif entry:
+            traffic_note = "kernel changed since the counters were taken"
+    roofline = {"bound": "hbm", "kernel": dom_kernel, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                "traffic_note": traffic_note, "algorithmic_bytes_per_launch": call_bytes[dom],
+                "avg_launch_us": round(per_call_us[dom], 2)}
+
+    # --------------------------------------------------------- CPU baseline --
+    cpu_baseline = None
+    if not args.no_cpu_baseline:
+        import oracle
+        model, ncpu = cpu_info()
+        r1 = min(args.cpu_mx_rows, M1)
+        r2 = min(args.cpu_group_rows, M2)
+        xb1 = np.ascontiguousarray(W.bf16_bits(x1_host)[:r1])
+        xb2 = np.ascontiguousarray(W.bf16_bits(x2_host)[:r2])
+        e16 = np.minimum(ends16, r2).astype(np.int32)
+        e128 = np.minimum(ends128, r2).astype(np.int32)
+        t0 = time.perf_counter()
+        q, s = oracle.mx_quantize(xb1)
+        y = oracle.mx_dequantize(q, s)
+        g16, sc16 = oracle.group_scale(xb2, e16, oracle.LAYOUT_ROW)
+        g128, sc128 = oracle.group_scale(xb2, e128, oracle.LAYOUT_COL)
+        g128t = oracle.transpose_u8(g128)
+        t1 = time.perf_counter()
+        sample_bytes = (2 * mx_bytes(r1, K1) + group_bytes(r2, K2, G_ROW) + group_bytes(r2, K2, G_COL)
+                        + transpose_bytes(r2, K2))
+        # the sample's rows were also computed by the GPU in the last step: same bytes?
+        b = sets[(args.warmup + args.steps - 1) % len(sets)]
+        same_mx = (np.array_equal(b.q1[:r1].cpu().numpy(), q) and np.array_equal(b.s1[:r1].cpu().numpy(), s)
+                   and np.array_equal(W.bf16_bits(b.y1[:r1].cpu()), y))
+        cpu_baseline = {
+            "value": round(sample_bytes / ((t1 - t0) * 1e9), 3), "unit": "GB/s", "cores": 1,
+            "kind": "oracle", "seconds": round(t1 - t0, 2),
+            "sample": (f"same five calls on the first {r1} of {M1} dispatch rows and the first {r2} of {M2} "
+                       f"token rows (group offsets cut at {r2}); one thread; algorithmic bytes of the sample "
+                       f"over wall time"),
+            "cpu_model": model, "host_cpus_available": ncpu,
+            "mx_sample_matches_gpu": bool(same_mx),
+        }
+
+    props = torch.cuda.get_device_properties(0)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16->e4m3",
+        "data": "synthetic",
+        "config": {
+            "workload": ("MoE float8 quantization step: MXFP8 quantize+dequantize of a (65536, 5120) bf16 "
+                         "dispatch payload, per-group fp8 scaling of (16640, 5120) bf16 tokens with 16 Zipf "
+                         "groups row-major and 128 groups column-major + transform to row-major"),
+            "dispatch_shape": list(DISPATCH), "tokens_shape": list(TOKENS),
+            "groups_row": G_ROW, "groups_col": G_COL, "rotated_buffer_sets": len(sets),
+            "step_algorithmic_bytes": step_bytes,
+        },
+        "frac_of_peak": round(value / HBM_PEAK_GBPS, 4),
+        "roofline": roofline,
+        "cpu_baseline": cpu_baseline,
+        "kernels": kernels,
+        "copy_ceiling_GBps": round(copy_gbps, 1),
+        "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""), "cus": props.multi_processor_count},
+        "host_ms_per_step": round(host_ms, 4), "device_ms_per_step": round(dev_ms, 4),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
