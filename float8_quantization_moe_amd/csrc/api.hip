@@ -88,6 +88,7 @@ static mxq_status check_group_sizes(int64_t M, int64_t K, int64_t G)
     if (st != MXQ_OK) return st;
     if (M > kGroupMaxRows || K > kGroupMaxK || K % 8 != 0) return MXQ_ERR_SHAPE;
     if (G < 1 || G > kGroupMaxG) return MXQ_ERR_SHAPE;
+    if (!mxq::group_scale_sizes_ok(M, K, G)) return MXQ_ERR_SHAPE;
     return MXQ_OK;
 }
 

@@ -11,6 +11,7 @@ namespace mxq {
 hipError_t launch_mx_quantize(const void* x, int64_t M, int64_t K, void* q, void* s, hipStream_t stream);
 hipError_t launch_mx_dequantize(const void* q, const void* s, int64_t M, int64_t K, void* y, hipStream_t stream);
 
+bool group_scale_sizes_ok(int64_t M, int64_t K, int64_t G);
 size_t group_scale_workspace_bytes(int64_t M, int64_t K, int32_t G);
 hipError_t launch_group_scale(const void* x, int M, int K, const int32_t* offs, int G, int layout,
                               void* q, float* scales, void* workspace, hipStream_t stream);

@@ -179,3 +179,28 @@ def test_transpose_shapes(R, C):
     got = U.host_u8(og.t)
     assert np.array_equal(got, a.T), U.first_mismatch(got, a.T)
     assert og.guard_intact()
+
+
+# The hold kernel keeps each tile on chip until its group's scales are known;
+# groups too large to hold, and tiles whose bounded wait runs out, go through
+# the deferred kernel.  Force both routes from the host and check the bytes.
+ROUTES = {
+    "held": {},
+    "all_streamed": {"MXQ_GROUP_HOLD_TILES": "0"},
+    "all_waits_time_out": {"MXQ_GROUP_WAIT_US": "0"},
+    "tiny_hold_limit": {"MXQ_GROUP_HOLD_TILES": "25"},
+}
+
+
+@pytest.mark.parametrize("route", list(ROUTES), ids=list(ROUTES))
+def test_hold_and_deferred_routes(route, monkeypatch):
+    for k, v in ROUTES[route].items():
+        monkeypatch.setenv(k, v)
+    M, K = 3000, 1040
+    rng = np.random.default_rng(31)
+    x = (rng.standard_normal((M, K)) * np.exp(rng.standard_normal((M, 1)))).astype(np.float32)
+    x_bits = (x.view(np.uint32) >> 16).astype(np.uint16)
+    x_bits[17, 5] = 0x7F80                 # a non-finite column in the first group
+    ends = _sizes_to_ends([1500, 0, 700, 3, 597, 200])   # all 3000 rows in groups
+    check_group(x_bits, ends, name=route)
+    check_group(x_bits, _sizes_to_ends([1000, 1000]), name=route + " with tail rows")
