@@ -86,8 +86,8 @@ static_assert(TileCfg<1>::NS * kHold == TileCfg<1>::R, "col tile shape");
 
 // ------------------------------------------------------------ workspace ---
 struct ChunkEntry {
-    int g, r0, r1, first;  // group (G: rows past the last end, -1: unused), rows, first chunk of the group
-    int count, pad0, pad1, pad2;  // chunks of the group
+    int g, r0, r1, first;      // group (G: rows past the last end, -1: unused), rows, first chunk of the group
+    int count, gr0, gr1, pad;  // chunks of the group, and the group's rows [gr0, gr1)
 };
 
 struct Workspace {
@@ -203,6 +203,7 @@ struct TileInfo {
     int g, r0, r1;        // group (G = rows past the last end) and its rows [r0, r1)
     int a;                // aligned first row of the tile (r0 rounded down to R)
     int first, count;     // the group's chunks: ids [first, first + count)
+    int gr0, gr1;         // the group's rows
     int j, s;             // chunk id and strip
 };
 
@@ -217,6 +218,8 @@ __device__ __forceinline__ TileInfo tile_info(const ChunkEntry* __restrict__ tab
     t.r1 = e0.z;
     t.first = e0.w;
     t.count = e1.x;
+    t.gr0 = e1.y;
+    t.gr1 = e1.z;
     t.a = (t.r0 / R) * R;
     t.j = j;
     t.s = s;
@@ -321,7 +324,7 @@ __device__ __forceinline__ void quantize_store_tile(const uint4 v[kHold], const 
             const int row = t.a + C::row(rs, i);
             if (row >= t.r0 && row < t.r1) {
                 const uint2 out = zero ? make_uint2(0, 0) : group_quantize_chunk(v[i], cs);
-                store_nt(out, (uint2*)(q + (int64_t)row * K + k));
+                *(uint2*)(q + (int64_t)row * K + k) = out;
             }
         }
     } else {
@@ -365,7 +368,7 @@ __device__ __forceinline__ void quantize_store_tile(const uint4 v[kHold], const 
             const uint4 val = *(const uint4*)(stage + col_tile_offset(cc, rb));
             uint8_t* dst = q + (col0 + cc) * (int64_t)M + t.a + rb;
             if (aligned16 && a == rb && e == rb + 16) {
-                store_nt(val, (uint4*)dst);
+                *(uint4*)dst = val;
             } else {
                 store_partial16(val, dst, a - rb, e - rb, aligned16);
             }
@@ -438,7 +441,9 @@ void group_plan_kernel(const int32_t* __restrict__ offs, int G, int M, int K, Wo
             e.r1 = sh_en[l] < a + (i + 1) * R ? sh_en[l] : a + (i + 1) * R;
             e.first = sh_first[l];
             e.count = sh_cnt[l];
-            e.pad0 = e.pad1 = e.pad2 = 0;
+            e.gr0 = sh_st[l];
+            e.gr1 = sh_en[l];
+            e.pad = 0;
             ws.table[c] = e;
         }
         // scales of this batch's empty groups
@@ -453,7 +458,7 @@ void group_plan_kernel(const int32_t* __restrict__ offs, int G, int M, int K, Wo
         ChunkEntry e;
         e.g = -1;
         e.r0 = e.r1 = e.first = e.count = 0;
-        e.pad0 = e.pad1 = e.pad2 = 0;
+        e.gr0 = e.gr1 = e.pad = 0;
         ws.table[c] = e;
     }
 }
@@ -482,7 +487,7 @@ template <int LAYOUT>
 __global__ __launch_bounds__(kTThreads)
 void group_hold_kernel(const uint16_t* __restrict__ x, int M, int K, int G, int S, int SB, int slots, Workspace ws,
                        float* __restrict__ scales, uint8_t* __restrict__ q, int hold_limit,
-                       unsigned long long timeout_ticks)
+                       unsigned long long timeout_ticks, int deferred_launched)
 {
     using C = TileCfg<LAYOUT>;
     __shared__ __align__(16) uint8_t stage[LAYOUT == 1 ? C::W * C::R : 16];
@@ -505,7 +510,9 @@ void group_hold_kernel(const uint16_t* __restrict__ x, int M, int K, int G, int 
         quantize_store_tile<LAYOUT>(v, cs, t, M, K, k, cg, rs, q, stage, true);
         return;
     }
-    const bool streamed = t.count * S > hold_limit;
+    // A (group, strip) is one synchronisation domain and its tiles are launched
+    // consecutively, so `count` tiles must be resident together.
+    const bool streamed = t.count > hold_limit;
     load_tile<LAYOUT>(x, K, t, k, rs, v);
 
     // Column maxima of this tile, published as one row of the partials by the
@@ -580,18 +587,36 @@ void group_hold_kernel(const uint16_t* __restrict__ x, int M, int K, int G, int 
                 if (wall_clock64() - t0 > timeout_ticks) break;
                 __builtin_amdgcn_s_sleep(2);
             }
-            if (!ok) {
+            if (!ok && deferred_launched) {
                 __hip_atomic_store(ws.deferred + (int64_t)j * S + s, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 __hip_atomic_store(ws.any, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
             order_acquire();
-            sh_state = ok ? 2 : 3;
+            sh_state = ok ? 2 : deferred_launched ? 3 : 4;
         }
         __syncthreads();
         if (sh_state == 3) return;                        // left for the deferred kernel
-        if (k < K)
+        if (sh_state == 4) {
+            // The wait ran out and no deferred pass follows: reduce this strip's
+            // maxima over all of the group's rows straight from the input (slow,
+            // only when the device cannot keep the group's tiles resident).
+            uint4 a = make_uint4(0, 0, 0, 0);
+            if (k < K)
+                for (int r = t.gr0 + rs; r < t.gr1; r += C::NS) max8(a, abs8(*(const uint4*)(x + (int64_t)r * K + k)));
+            red[rs][cg] = a;
+            __syncthreads();
+            if (rs == 0) {
+#pragma unroll
+                for (int r = 1; r < C::NS; ++r) max8(a, red[r][cg]);
+                *(float4*)(sh_scale + cg * 8) = scales_lo(a);
+                *(float4*)(sh_scale + cg * 8 + 4) = scales_hi(a);
+            }
+            __syncthreads();
+            cs = make_col_scales(*(const float4*)(sh_scale + cg * 8), *(const float4*)(sh_scale + cg * 8 + 4));
+        } else if (k < K) {
             cs = make_col_scales(bits_f4(load_coherent(scales + (int64_t)t.g * K + k)),
                                  bits_f4(load_coherent(scales + (int64_t)t.g * K + k + 4)));
+        }
     }
     quantize_store_tile<LAYOUT>(v, cs, t, M, K, k, cg, rs, q, stage, false);
 }
@@ -612,7 +637,7 @@ void group_deferred_kernel(const uint16_t* __restrict__ x, int M, int K, int G, 
         const int j = tile / S, s = tile % S;
         const TileInfo t = tile_info<C::R>(ws.table, j, s);
         if (t.g < 0 || t.g == G) continue;
-        const bool streamed = t.count * S > hold_limit;
+        const bool streamed = t.count > hold_limit;
         if (!streamed && ws.deferred[(int64_t)j * S + s] == 0u) continue;
         const int cg = (int)threadIdx.x % C::CG, rs = (int)threadIdx.x / C::CG;
         const int k = s * C::W + cg * 8;
@@ -675,9 +700,14 @@ static hipError_t launch_layout(const void* x, int M, int K, const int32_t* offs
     hipLaunchKernelGGL(group_plan_kernel<C::R>, dim3(64), dim3(kGThreads), 0, stream, offs, G, M, K, ws, nGS,
                        (int)nTiles, (int)slots, scales);
     if (M > 0) {
+        // No group spans more than ceil(M/R) + 1 chunks: unless that exceeds the
+        // hold limit nothing is streamed, and tiles whose wait runs out finish
+        // themselves, so the deferred pass is not launched at all.
+        const int deferred = (int64_t)(M + C::R - 1) / C::R + 1 > hold_limit ? 1 : 0;
         hipLaunchKernelGGL(group_hold_kernel<LAYOUT>, dim3((unsigned)nTiles), dim3(kTThreads), 0, stream,
                            (const uint16_t*)x, M, K, G, S, SB, (int)slots, ws, scales, (uint8_t*)q, hold_limit,
-                           timeout_ticks);
+                           timeout_ticks, deferred);
+        if (!deferred) return hipGetLastError();
         const int dgrid = (int)(nTiles < 512 ? nTiles : 512);
         hipLaunchKernelGGL(group_deferred_kernel<LAYOUT>, dim3((unsigned)dgrid), dim3(kTThreads), 0, stream,
                            (const uint16_t*)x, M, K, G, S, ws, (const float*)scales, (uint8_t*)q, hold_limit,

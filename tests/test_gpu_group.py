@@ -187,8 +187,13 @@ def test_transpose_shapes(R, C):
 ROUTES = {
     "held": {},
     "all_streamed": {"MXQ_GROUP_HOLD_TILES": "0"},
+    # no deferred pass is launched for these sizes: timed-out tiles finish themselves
     "all_waits_time_out": {"MXQ_GROUP_WAIT_US": "0"},
-    "tiny_hold_limit": {"MXQ_GROUP_HOLD_TILES": "25"},
+    # groups of more than 5 chunks streamed, smaller ones held
+    "small_hold_limit": {"MXQ_GROUP_HOLD_TILES": "5"},
+    # deferred pass launched and every waiting tile defers to it
+    "time_outs_deferred": {"MXQ_GROUP_HOLD_TILES": "5", "MXQ_GROUP_WAIT_US": "0"},
+    "launch_order_strip_fastest": {"MXQ_GROUP_STRIP_BLOCK": "2"},
 }
 
 
