@@ -3,7 +3,7 @@
 //
 // "[mxfp8 MoE training] Support mxfp8 all to all in expert parallel", Summary:
 // the payload is quantized to mxfp8 (e4m3 data + e8m0 scales), both buffers are
-// exchanged, and the receiver dequantizes back to the original precision.  The
+// exchanged, and the receiver decodes them back into bf16, the input precision.  The
 // kernels below produce / consume exactly those two buffers.
 //
 // Both kernels are flat streaming passes over M*K elements (an HBM-bound byte

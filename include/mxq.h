@@ -6,7 +6,7 @@
  *   "[mxfp8 MoE training] Support mxfp8 all to all in expert parallel"
  *   (torchtitan PR 1765), Summary: the expert-parallel all-to-all payload is
  *   quantized to mxfp8, the e4m3 data and the e8m0 scales travel in two
- *   all_to_all_single calls, and the receiver dequantizes back to the original
+ *   all_to_all_single calls, and the receiver decodes them back to the input's
  *   precision.  mxq_quantize_mx / mxq_dequantize_mx are the two ends of that
  *   exchange; the buffers they produce and consume are exactly the ones sent.
  *
@@ -81,7 +81,8 @@ int mxq_last_hip_error(void);
 /*
  * MXFP8 quantization of one all-to-all payload.
  * Source: "[mxfp8 MoE training] Support mxfp8 all to all in expert parallel",
- * Summary (quantize the inputs to mxfp8; e4m3 data; e8m0 scales).
+ * Summary (the payload is encoded as MXFP8 before the exchange: an e4m3 buffer
+ * and an e8m0 buffer).
  *
  *   x_bf16  (M, K) bf16 input, row-major.
  *   q_e4m3  (M, K) uint8 output: e4m3 codes, row-major (the "e4m3 data" buffer).
@@ -94,7 +95,7 @@ int mxq_last_hip_error(void);
  * saturating at +-448, sign kept (-0 -> 0x80).  A block containing Inf or NaN
  * gets scale 0xFF and every code 0x7F.
  *
- * Requires K % 32 == 0 (MXQ_ERR_SHAPE), M >= 0, K >= 0, M*K < 2^62.
+ * Requires K % 32 == 0 (MXQ_ERR_SHAPE), M >= 0, K >= 0, M*K <= 2^40.
  * M == 0 or K == 0 is a no-op that returns MXQ_OK.  A token-row split of Q and S
  * (the all-to-all's input splits) keeps every block whole.
  */
@@ -104,7 +105,7 @@ mxq_status mxq_quantize_mx(const void* x_bf16, int64_t M, int64_t K,
 /*
  * MXFP8 dequantization of one received payload back to bf16.
  * Source: "[mxfp8 MoE training] Support mxfp8 all to all in expert parallel",
- * Summary (dequantize outputs back to original precision).
+ * Summary (after the exchange the receiver decodes both buffers back to bf16).
  *
  *   q_e4m3  (M, K) uint8 e4m3 codes; s_e8m0 (M, K/32) uint8 e8m0 codes, both as
  *           produced by mxq_quantize_mx (or received from a peer).
@@ -120,8 +121,9 @@ mxq_status mxq_dequantize_mx(const void* q_e4m3, const void* s_e8m0, int64_t M, 
 
 /*
  * Bytes of device workspace mxq_group_scale_fp8 needs for these sizes (0 for
- * invalid sizes).  The workspace holds per-chunk partial maxima; its contents
- * need no initialisation and are meaningless after the call.
+ * invalid sizes).  The workspace holds the call's chunk table, per-chunk column
+ * maxima and arrival counters; its contents need no initialisation, are
+ * meaningless after the call, and two calls in flight at once must not share it.
  */
 size_t mxq_group_scale_workspace_bytes(int64_t M, int64_t K, int32_t G);
 
@@ -152,8 +154,9 @@ size_t mxq_group_scale_workspace_bytes(int64_t M, int64_t K, int32_t G);
  * binary32 product x*s, nearest, ties to even, saturating at +-448.  An empty
  * group has amax 0.  A column holding Inf or NaN gets s = NaN and q = 0x7F.
  *
- * Requires K % 8 == 0, 0 <= M < 2^31, K < 2^31 (MXQ_ERR_SHAPE), G >= 1.  K == 0
- * is a no-op; M == 0 still writes the (G, K) scales.
+ * Requires K % 8 == 0, 0 <= M <= 2^31 - 1024, K <= 2^23, 1 <= G <= 2^20, and
+ * the tile count (about (M/128 + G) * K/512) below 2^31 (MXQ_ERR_SHAPE otherwise).
+ * K == 0 is a no-op; M == 0 still writes the (G, K) scales.
  */
 mxq_status mxq_group_scale_fp8(const void* x_bf16, int64_t M, int64_t K,
                                const int32_t* group_end_offs, int32_t G, int out_layout,
@@ -165,7 +168,7 @@ mxq_status mxq_group_scale_fp8(const void* x_bf16, int64_t M, int64_t K,
  * transform between the two outputs of mxq_group_scale_fp8.
  * Source: "[moe training] fix uncoalesced global accesses in per group rowwise
  * scaling kernel", Summary (write one layout, then transform to the other).
- * Any R, C >= 0 (R*C < 2^62); R == 0 or C == 0 is a no-op; in and out must not
+ * Any R, C >= 0 with R*C <= 2^40; R == 0 or C == 0 is a no-op; in and out must not
  * overlap.
  */
 mxq_status mxq_transpose_u8(const void* in, int64_t R, int64_t C, void* out, void* stream);

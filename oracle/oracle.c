@@ -11,8 +11,8 @@
  * Sources (the pages this follows):
  *   [A2A]  "[mxfp8 MoE training] Support mxfp8 all to all in expert parallel"
  *          (torchtitan PR 1765), Summary: the payload is quantized to mxfp8,
- *          e4m3 data and e8m0 scales are exchanged, then dequantized back to the
- *          original precision.
+ *          e4m3 data and e8m0 scales are exchanged, and the receiver turns them
+ *          back into bf16, the input's precision.
  *   [GRP]  "[moe training] fix uncoalesced global accesses in per group rowwise
  *          scaling kernel" (torchao PR 2761), Summary: per-group float8 scaling
  *          whose output feeds the LHS of a scaled grouped GEMM, written row-major
