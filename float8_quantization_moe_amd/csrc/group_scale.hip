@@ -16,34 +16,35 @@
 // at the same rate as a cold read on MI355X (the last-level cache does not turn
 // the second pass into a cheap one).  So the input is read ONCE and held on chip:
 //
-//   plan   build the chunk table, zero the per-(group, strip) arrival counters,
-//          ready flags and per-tile "deferred" marks, and write the scales of
-//          empty groups.
+//   plan   build the chunk table and empty-group flags, zero the per-(group,
+//          strip) arrival counters and per-tile "deferred" marks, and fill the
+//          partial maxima and the scales with values no result takes ("not yet
+//          written").
 //   hold   one workgroup per tile (a 128-row chunk of one group x 512 columns).
 //          It loads its tile into registers, reduces the column maxima (packed
 //          16-bit max of |bf16 bits| -- positive bf16 order is integer order and
 //          Inf/NaN sort above every finite value), publishes them as one row of
 //          partial maxima, and counts itself in.  The last tile of a (group,
-//          strip) to arrive reduces the strip's partial rows, divides, writes
-//          the (G, K) scales and raises the strip's ready flag; the others wait
-//          for the flag (bounded by a wall-clock limit) and then quantize the
-//          tile still in their registers: 2 bytes read + 1 byte written per
-//          element, nothing else.  (Folding the maxima with atomic max instead
-//          was measured slower: every tile of a strip hits the same addresses.)
+//          strip) to arrive reduces the strip's partial rows, divides and writes
+//          the (G, K) scales; the others poll their scales until written
+//          (bounded by a wall-clock limit) and then quantize the tile still in
+//          their registers: 2 bytes read + 1 byte written per element, nothing
+//          else.  (Folding the maxima with atomic max instead was measured
+//          slower: every tile of a strip hits the same addresses.)
 //   deferred  tiles of groups too large to hold on chip at once (more tiles than
 //          the device can keep resident), and tiles whose wait ran out, are
 //          re-read and quantized here after the hold kernel has finished, so the
 //          result never depends on how many workgroups are resident.
 //
-// Cross-workgroup data (partial maxima, scales, counters, flags) crosses XCDs,
-// whose L2 caches are not coherent with each other.  An agent-scope fence would
-// write back and invalidate the whole L2 at every publish and every wake-up,
-// which costs microseconds each on MI355X; instead every such access is a
-// relaxed agent-scope atomic (it goes through the caches to the coherence
-// point), and ordering between them comes from waiting for the wave's memory
-// operations to complete (s_waitcnt vmcnt(0)) with a workgroup-scope fence to
-// keep the compiler from moving accesses across.  Ordinary cached accesses are
-// used only for data that no other workgroup of the same launch reads.
+// Cross-workgroup data (partial maxima, scales, counters) crosses XCDs, whose
+// L2 caches are not coherent with each other.  An agent-scope fence would write
+// back and invalidate the whole L2 at every publish and every wake-up, which
+// costs microseconds each on MI355X; instead every such access is a relaxed
+// agent-scope atomic (it goes through the caches to the coherence point), and
+// since each partial row and each scale is polled until it holds a written
+// value, no ordering between different addresses is needed at all (no fence,
+// no flag, no wait for a store to complete).  Ordinary cached accesses are used
+// only for data that no other workgroup of the same launch writes.
 //
 // Row chunks never cross a group boundary and are cut at multiples of the tile
 // height, so interior tiles are aligned in both output layouts.  The plan kernel
@@ -55,6 +56,7 @@
 // column, staged as a 512 x 128-byte transposed tile in LDS, written as 128
 // contiguous bytes per output row.
 #include <stdlib.h>
+#include <string.h>
 
 #include "device_common.hpp"
 #include "internal.hpp"
@@ -84,6 +86,14 @@ struct TileCfg<1> {                 // column-major output
 static_assert(TileCfg<0>::NS * kHold == TileCfg<0>::R, "row tile shape");
 static_assert(TileCfg<1>::NS * kHold == TileCfg<1>::R, "col tile shape");
 
+// Values that no finished result takes: a scale is a positive float or the
+// canonical NaN 0x7FC00000, a column maximum of |bf16| bits is at most 0x7FFF.
+// The plan kernel fills the partial maxima and the scales with them, and a
+// reader polls the datum itself until it is written, so no flag and no
+// ordering between different addresses is needed.
+constexpr uint32_t kScaleUnset = 0xFFFFFFFFu;
+constexpr uint16_t kPartialUnset = 0xFFFFu;
+
 // ------------------------------------------------------------ workspace ---
 struct ChunkEntry {
     int g, r0, r1, first;      // group (G: rows past the last end, -1: unused), rows, first chunk of the group
@@ -94,7 +104,9 @@ struct Workspace {
     ChunkEntry* table;    // [slots] one entry per chunk id
     uint16_t* partial;    // [slots][K] column maxima of each chunk (|bf16 bits|)
     uint32_t* count;      // [G][S] arrivals per (group, strip)
-    uint32_t* ready;      // [G][S] 1 once the strip's scales are written
+    uint32_t* empty;      // [G] 1 if the group has no rows
+    int32_t* gend;        // [G] end row of each group (offsets clamped as documented)
+    int32_t* bfirst;      // [ceil(M/128)] group containing the first row of each 128-row block (G: none)
     uint32_t* deferred;   // [slots][S] 1 if the tile was left for the deferred kernel
     uint32_t* any;        // [1] 1 if any tile needs the deferred kernel
 };
@@ -104,7 +116,7 @@ static size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 static int64_t chunk_slots(int64_t M, int R, int64_t G) { return (M + R - 1) / R + G + 1; }
 
 template <int LAYOUT>
-static size_t workspace_layout(int64_t M, int64_t K, int64_t G, size_t off[6])
+static size_t workspace_layout(int64_t M, int64_t K, int64_t G, size_t off[8])
 {
     using C = TileCfg<LAYOUT>;
     const int64_t slots = chunk_slots(M, C::R, G);
@@ -113,9 +125,11 @@ static size_t workspace_layout(int64_t M, int64_t K, int64_t G, size_t off[6])
     off[0] = o; o += align256((size_t)(slots * sizeof(ChunkEntry)));
     off[1] = o; o += align256((size_t)(slots * K * 2));
     off[2] = o; o += align256((size_t)(G * S * 4));
-    off[3] = o; o += align256((size_t)(G * S * 4));
+    off[3] = o; o += align256((size_t)(G * 4));
     off[4] = o; o += align256((size_t)(slots * S * 4));
     off[5] = o; o += 256;
+    off[6] = o; o += align256((size_t)(G * 4));
+    off[7] = o; o += align256((size_t)(((M + 127) / 128 + 1) * 4));
     return o;
 }
 
@@ -125,12 +139,15 @@ bool group_scale_sizes_ok(int64_t M, int64_t K, int64_t G)
     const int64_t lim = ((int64_t)1 << 31) - 1;
     const int64_t tiles_row = chunk_slots(M, TileCfg<0>::R, G) * ((K + TileCfg<0>::W - 1) / TileCfg<0>::W);
     const int64_t tiles_col = chunk_slots(M, TileCfg<1>::R, G) * ((K + TileCfg<1>::W - 1) / TileCfg<1>::W);
-    return tiles_row <= lim && tiles_col <= lim && (int64_t)M * K / 8 <= lim * 64;
+    // (and the plan kernel's fills, counted in 16-byte units)
+    const int64_t fill_partial = chunk_slots(M, TileCfg<0>::R, G) * K / 8;
+    return tiles_row <= lim && tiles_col <= lim && fill_partial <= lim && G * K / 4 <= lim &&
+           (int64_t)M * K / 8 <= lim * 64;
 }
 
 size_t group_scale_workspace_bytes(int64_t M, int64_t K, int32_t G)
 {
-    size_t off[6];
+    size_t off[8];
     const size_t a = workspace_layout<0>(M, K, G, off);
     const size_t b = workspace_layout<1>(M, K, G, off);
     return a > b ? a : b;
@@ -228,8 +245,8 @@ __device__ __forceinline__ TileInfo tile_info(const ChunkEntry* __restrict__ tab
 
 // ---------------------------------------------------- coherent accesses ---
 // Relaxed agent-scope atomics: each access reaches the coherence point shared by
-// all XCDs.  Ordering between them: order_release() before the access that
-// signals, order_acquire() after the access that observed the signal.
+// all XCDs, so a value written by a workgroup on one XCD is eventually seen by
+// a workgroup polling it on another.
 __device__ __forceinline__ void store_coherent(uint4 v, void* p)
 {
     unsigned long long* q = (unsigned long long*)p;
@@ -245,20 +262,21 @@ __device__ __forceinline__ uint4 load_coherent(const void* p)
     return make_uint4((uint32_t)a, (uint32_t)(a >> 32), (uint32_t)b, (uint32_t)(b >> 32));
 }
 
-// vmcnt(0), expcnt and lgkmcnt left at their maxima: wait for this wave's
-// outstanding vector memory operations only.
-constexpr int kWaitVmem = 0 | (0x7 << 4) | (0xF << 8);
+// ------------------------------------------------------ buffer accesses ---
+// Raw buffer loads through a (base, size) resource: an offset at or past the
+// size reads zero without touching memory.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr uint32_t kOOB = 0xFFFFFFF0u;      // above every resource size used here (at most 2^31)
 
-__device__ __forceinline__ void order_release()
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes)
 {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_s_waitcnt(kWaitVmem);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-__device__ __forceinline__ void order_acquire()
+__device__ __forceinline__ uint4 buf_load16(Rsrc r, uint32_t off)
 {
-    __builtin_amdgcn_s_waitcnt(kWaitVmem);
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
 }
 
 // Load this lane's 16 rows x 8 columns of the tile (zeros outside rows/columns).
@@ -267,12 +285,18 @@ __device__ __forceinline__ void load_tile(const uint16_t* __restrict__ x, int K,
                                           uint4 v[kHold])
 {
     using C = TileCfg<LAYOUT>;
-    const bool kin = k < K;
+    // Raw buffer loads over rows [a, r1) of the tile (at most 128 rows x 2^24
+    // bytes): rows past r1 fall outside the resource and rows before r0 or
+    // columns past K get an offset outside it, and such loads read zero with no
+    // memory traffic.  Masking by offset instead of by branch lets all kHold
+    // loads be in flight at once.
+    const Rsrc r = make_rsrc(x + (int64_t)t.a * K, (uint32_t)(t.r1 - t.a) * (uint32_t)K * 2u);
+    const int lo = t.r0 - t.a;
 #pragma unroll
     for (int i = 0; i < kHold; ++i) {
-        const int row = t.a + C::row(rs, i);
-        v[i] = (kin && row >= t.r0 && row < t.r1) ? *(const uint4*)(x + (int64_t)row * K + k)
-                                                  : make_uint4(0, 0, 0, 0);
+        const int rt = C::row(rs, i);
+        const uint32_t off = (k < K && rt >= lo) ? ((uint32_t)rt * (uint32_t)K + (uint32_t)k) * 2u : kOOB;
+        v[i] = buf_load16(r, off);
     }
 }
 
@@ -377,19 +401,24 @@ __device__ __forceinline__ void quantize_store_tile(const uint4 v[kHold], const 
 }
 
 // ---------------------------------------------------------------- plan ----
-// Every block clears counters, ready flags and deferred marks; block 0 also
-// writes the chunk table (and marks unused slots) and the scales of empty groups.
+// Every block clears counters and deferred marks and fills the partial maxima
+// (and, when there are rows, the scales) with their "not yet written" values;
+// block 0 writes the chunk table (marking unused slots) and the empty-group
+// flags, and when there are no rows at all it writes every group's scales
+// (otherwise the hold kernel writes the scales of empty groups).
 template <int R>
 __global__ __launch_bounds__(kGThreads)
 void group_plan_kernel(const int32_t* __restrict__ offs, int G, int M, int K, Workspace ws, int nGS, int nTiles,
-                       int slots, float* __restrict__ scales)
+                       int slots, float* __restrict__ scales, int nPartial16, int nScale16)
 {
     const int tid = (int)(blockIdx.x * blockDim.x + threadIdx.x);
     const int stride = (int)(gridDim.x * blockDim.x);
-    for (int i = tid; i < nGS; i += stride) {
-        ws.count[i] = 0;
-        ws.ready[i] = 0;
-    }
+    const uint32_t pu = (uint32_t)kPartialUnset * 0x10001u;
+    const uint4 p_unset = make_uint4(pu, pu, pu, pu);
+    const uint4 s_unset = make_uint4(kScaleUnset, kScaleUnset, kScaleUnset, kScaleUnset);
+    for (int i = tid; i < nPartial16; i += stride) ((uint4*)ws.partial)[i] = p_unset;
+    for (int i = tid; i < nScale16; i += stride) ((uint4*)scales)[i] = s_unset;
+    for (int i = tid; i < nGS; i += stride) ws.count[i] = 0;
     for (int i = tid; i < nTiles; i += stride) ws.deferred[i] = 0;
     if (tid == 0) *ws.any = 0;
     if (blockIdx.x != 0) return;
@@ -416,6 +445,13 @@ void group_plan_kernel(const int32_t* __restrict__ offs, int G, int M, int K, Wo
             sh_en[lane] = e;
             sh_first[lane] = incl - cnt;
             sh_cnt[lane] = cnt;
+            if (g < G) {
+                ws.empty[g] = e <= st ? 1u : 0u;
+                ws.gend[g] = e;
+            }
+            // 128-row blocks whose first row is in this group (or past the last end)
+            if (g <= G)
+                for (int c = (st + 127) / 128; c * 128 < e; ++c) ws.bfirst[c] = g;
             const unsigned long long m = __ballot(g < G && e <= st);
             if (lane == 0) {
                 sh_empty = m;
@@ -446,11 +482,13 @@ void group_plan_kernel(const int32_t* __restrict__ offs, int G, int M, int K, Wo
             e.pad = 0;
             ws.table[c] = e;
         }
-        // scales of this batch's empty groups
-        for (unsigned long long mm = sh_empty; mm; mm &= mm - 1) {
-            const int g = base + __builtin_ctzll(mm);
-            for (int k = (int)threadIdx.x * 4; k < K; k += kGThreads * 4)
-                *(float4*)(scales + (int64_t)g * K + k) = make_float4(s_empty, s_empty, s_empty, s_empty);
+        // with no rows every group is empty and no hold kernel runs: write the scales here
+        if (M == 0) {
+            for (unsigned long long mm = sh_empty; mm; mm &= mm - 1) {
+                const int g = base + __builtin_ctzll(mm);
+                for (int k = (int)threadIdx.x * 4; k < K; k += kGThreads * 4)
+                    *(float4*)(scales + (int64_t)g * K + k) = make_float4(s_empty, s_empty, s_empty, s_empty);
+            }
         }
         __syncthreads();
     }
@@ -482,6 +520,155 @@ __device__ __forceinline__ float4 bits_f4(uint4 u)
     return make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w));
 }
 
+// (kPartialUnset has the top bit set, which no |bf16| maximum has.)
+__device__ __forceinline__ bool partial_written(uint4 w)
+{
+    static_assert(kPartialUnset & 0x8000u, "unset marker");
+    return ((w.x | w.y | w.z | w.w) & 0x80008000u) == 0u;
+}
+__device__ __forceinline__ bool scales_written(uint4 a, uint4 b)
+{
+    return a.x != kScaleUnset && a.y != kScaleUnset && a.z != kScaleUnset && a.w != kScaleUnset &&
+           b.x != kScaleUnset && b.y != kScaleUnset && b.z != kScaleUnset && b.w != kScaleUnset;
+}
+
+// Column maxima of this lane's 8 columns over the group's rows gr0 + rs,
+// gr0 + rs + ns, ..., read from the input; only used when a wait ran out.
+__device__ __forceinline__ uint4 strip_max_from_x(const uint16_t* __restrict__ x, int K, const TileInfo& t, int k,
+                                                  int rs, int ns)
+{
+    uint4 a = make_uint4(0, 0, 0, 0);
+    if (k < K)
+        for (int r = t.gr0 + rs; r < t.gr1; r += ns) max8(a, abs8(*(const uint4*)(x + (int64_t)r * K + k)));
+    return a;
+}
+
+// ------------------------------------------------------- shared pieces ----
+template <int LAYOUT, bool STAGE = true>
+struct TileShared {
+    // (the column-layout staging tile only where a kernel stores q)
+    __align__(16) uint8_t stage[LAYOUT == 1 && STAGE ? TileCfg<LAYOUT>::W * TileCfg<LAYOUT>::R : 16];
+    uint4 red[TileCfg<LAYOUT>::NS][TileCfg<LAYOUT>::CG];
+    __align__(16) float scale[TileCfg<LAYOUT>::W];
+    int state;
+};
+
+// Tile of workgroup `blk`: blocks of SB strips, chunks within a block, strips
+// within that (SB = 1: chunk-fastest, so a (group, strip)'s tiles are launched
+// back to back).
+__device__ __forceinline__ void tile_of_block(int blk, int slots, int SB, int& j, int& s)
+{
+    const int per_block = slots * SB;
+    const int sb = blk / per_block, rem = blk % per_block;
+    j = rem / SB;
+    s = sb * SB + rem % SB;
+}
+
+// The first G workgroups also write the scales of an empty group (nothing
+// reads them during the launch).
+__device__ __forceinline__ void write_empty_group_scales(int G, int K, const Workspace& ws, float* __restrict__ scales,
+                                                         int nthreads)
+{
+    if ((int)blockIdx.x < G && ws.empty[blockIdx.x] != 0u) {
+        const float s_empty = group_scale_of(0u);
+        for (int kk = (int)threadIdx.x * 4; kk < K; kk += nthreads * 4)
+            *(float4*)(scales + (int64_t)blockIdx.x * K + kk) = make_float4(s_empty, s_empty, s_empty, s_empty);
+    }
+}
+
+// Column maxima of the held tile, published as one row of the partials by the
+// lanes with rs == 0 (all in wave 0), then the tile counts itself in.  No
+// ordering between the two is needed: the partial row carries its own "not yet
+// written" value and the last arrival polls it.  Returns 1 in every lane of
+// the last tile of its (group, strip) to arrive.
+template <int LAYOUT, class Sh>
+__device__ __forceinline__ int publish_and_count(const uint4 v[kHold], const TileInfo& t, int j, int s, int K, int S,
+                                                 int k, int cg, int rs, const Workspace& ws, bool streamed, Sh& sh)
+{
+    using C = TileCfg<LAYOUT>;
+    uint4 m = abs8(v[0]);
+#pragma unroll
+    for (int i = 1; i < kHold; ++i) max8(m, abs8(v[i]));
+    sh.red[rs][cg] = m;
+    __syncthreads();
+    if (rs == 0) {
+#pragma unroll
+        for (int r = 1; r < C::NS; ++r) max8(m, sh.red[r][cg]);
+        if (k < K) store_coherent(m, ws.partial + (int64_t)j * K + k);
+    }
+    if (threadIdx.x == 0) {
+        const uint32_t old = __hip_atomic_fetch_add(ws.count + (int64_t)t.g * S + s, 1u, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+        if (streamed) __hip_atomic_store(ws.any, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        sh.state = (old + 1 == (uint32_t)t.count) ? 1 : 0;
+    }
+    __syncthreads();
+    return sh.state;
+}
+
+// Last arrival: reduce the strip's partial rows over the group's chunks (each
+// polled until written; if one never comes, from the input instead), divide,
+// store the scales (`scales_coherent`: with agent-scope stores, for readers in
+// the same launch) and leave this lane's 8 scales in `cs`.
+template <int LAYOUT, class Sh>
+__device__ __forceinline__ void reduce_strip(const uint16_t* __restrict__ x, const TileInfo& t, int K, int k, int cg,
+                                             int rs, const Workspace& ws, float* __restrict__ scales,
+                                             bool scales_coherent, unsigned long long timeout_ticks, Sh& sh,
+                                             ColScales& cs)
+{
+    using C = TileCfg<LAYOUT>;
+    uint4 a = make_uint4(0, 0, 0, 0);
+    int ok = 1;
+    if (k < K) {
+        const uint16_t* p = ws.partial + (int64_t)t.first * K + k;
+        for (int c0 = rs; c0 < t.count; c0 += 4 * C::NS) {
+            uint4 b[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                b[u] = c0 + u * C::NS < t.count ? load_coherent(p + (int64_t)(c0 + u * C::NS) * K) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                if (!partial_written(b[u])) {
+                    const unsigned long long t0 = wall_clock64();
+                    while (true) {
+                        __builtin_amdgcn_s_sleep(1);
+                        b[u] = load_coherent(p + (int64_t)(c0 + u * C::NS) * K);
+                        if (partial_written(b[u])) break;
+                        if (wall_clock64() - t0 > timeout_ticks) {
+                            ok = 0;
+                            b[u] = make_uint4(0, 0, 0, 0);
+                            break;
+                        }
+                    }
+                }
+                max8(a, b[u]);
+            }
+        }
+    }
+    if (__syncthreads_or(!ok)) a = strip_max_from_x(x, K, t, k, rs, C::NS);   // a partial never came
+    sh.red[rs][cg] = a;
+    __syncthreads();
+    if (rs == 0) {
+#pragma unroll
+        for (int r = 1; r < C::NS; ++r) max8(a, sh.red[r][cg]);
+        const float4 lo = scales_lo(a), hi = scales_hi(a);
+        *(float4*)(sh.scale + cg * 8) = lo;
+        *(float4*)(sh.scale + cg * 8 + 4) = hi;
+        if (k < K) {
+            float* dst = scales + (int64_t)t.g * K + k;
+            if (scales_coherent) {
+                store_coherent(f4_bits(lo), dst);
+                store_coherent(f4_bits(hi), dst + 4);
+            } else {
+                *(float4*)dst = lo;
+                *(float4*)(dst + 4) = hi;
+            }
+        }
+    }
+    __syncthreads();
+    cs = make_col_scales(*(const float4*)(sh.scale + cg * 8), *(const float4*)(sh.scale + cg * 8 + 4));
+}
+
 // ---------------------------------------------------------------- hold ----
 template <int LAYOUT>
 __global__ __launch_bounds__(kTThreads)
@@ -490,15 +677,10 @@ void group_hold_kernel(const uint16_t* __restrict__ x, int M, int K, int G, int 
                        unsigned long long timeout_ticks, int deferred_launched)
 {
     using C = TileCfg<LAYOUT>;
-    __shared__ __align__(16) uint8_t stage[LAYOUT == 1 ? C::W * C::R : 16];
-    __shared__ uint4 red[C::NS][C::CG];
-    __shared__ __align__(16) float sh_scale[C::W];
-    __shared__ int sh_state;
-
-    // Launch order: blocks of SB strips, chunks within a block, strips within that.
-    const int per_block = slots * SB;
-    const int sb = (int)blockIdx.x / per_block, rem = (int)blockIdx.x % per_block;
-    const int j = rem / SB, s = sb * SB + rem % SB;
+    __shared__ TileShared<LAYOUT> sh;
+    int j, s;
+    tile_of_block((int)blockIdx.x, slots, SB, j, s);
+    write_empty_group_scales(G, K, ws, scales, kTThreads);
     const TileInfo t = tile_info<C::R>(ws.table, j, s);
     if (t.g < 0) return;                                  // unused chunk id (uniform)
     const int cg = (int)threadIdx.x % C::CG, rs = (int)threadIdx.x / C::CG;
@@ -507,7 +689,7 @@ void group_hold_kernel(const uint16_t* __restrict__ x, int M, int K, int G, int 
     uint4 v[kHold];
 
     if (t.g == G) {                                       // rows past the last end: zeros
-        quantize_store_tile<LAYOUT>(v, cs, t, M, K, k, cg, rs, q, stage, true);
+        quantize_store_tile<LAYOUT>(v, cs, t, M, K, k, cg, rs, q, sh.stage, true);
         return;
     }
     // A (group, strip) is one synchronisation domain and its tiles are launched
@@ -515,110 +697,212 @@ void group_hold_kernel(const uint16_t* __restrict__ x, int M, int K, int G, int 
     const bool streamed = t.count > hold_limit;
     load_tile<LAYOUT>(x, K, t, k, rs, v);
 
-    // Column maxima of this tile, published as one row of the partials by the
-    // lanes with rs == 0 -- all in wave 0, like the lane that then counts the
-    // tile in, so one wave-wide wait orders the publish before the count.
-    uint4 m = abs8(v[0]);
-#pragma unroll
-    for (int i = 1; i < kHold; ++i) max8(m, abs8(v[i]));
-    red[rs][cg] = m;
-    __syncthreads();
-    if (rs == 0) {
-#pragma unroll
-        for (int r = 1; r < C::NS; ++r) max8(m, red[r][cg]);
-        if (k < K) store_coherent(m, ws.partial + (int64_t)j * K + k);
-        order_release();
-    }
-    if (threadIdx.x == 0) {
-        const uint32_t old = __hip_atomic_fetch_add(ws.count + (int64_t)t.g * S + s, 1u, __ATOMIC_RELAXED,
-                                                    __HIP_MEMORY_SCOPE_AGENT);
-        if (streamed) __hip_atomic_store(ws.any, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        order_acquire();
-        sh_state = (old + 1 == (uint32_t)t.count) ? 1 : 0;   // 1: last to arrive
-    }
-    __syncthreads();
-
-    if (sh_state == 1) {
-        // last arrival: reduce the strip's partial rows over the group's chunks, divide
-        uint4 a = make_uint4(0, 0, 0, 0);
-        if (k < K) {
-            const uint16_t* p = ws.partial + (int64_t)t.first * K + k;
-            int c = rs;
-            for (; c + 3 * C::NS < t.count; c += 4 * C::NS) {
-                uint4 b[4];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) b[u] = load_coherent(p + (int64_t)(c + u * C::NS) * K);
-#pragma unroll
-                for (int u = 0; u < 4; ++u) max8(a, b[u]);
-            }
-            for (; c < t.count; c += C::NS) max8(a, load_coherent(p + (int64_t)c * K));
-        }
-        red[rs][cg] = a;
-        __syncthreads();
-        if (rs == 0) {
-#pragma unroll
-            for (int r = 1; r < C::NS; ++r) max8(a, red[r][cg]);
-            const float4 lo = scales_lo(a), hi = scales_hi(a);
-            *(float4*)(sh_scale + cg * 8) = lo;
-            *(float4*)(sh_scale + cg * 8 + 4) = hi;
-            if (k < K) {
-                store_coherent(f4_bits(lo), scales + (int64_t)t.g * K + k);
-                store_coherent(f4_bits(hi), scales + (int64_t)t.g * K + k + 4);
-            }
-            order_release();                              // scales complete before the flag
-        }
-        if (threadIdx.x == 0)      // same wave as the scale stores above
-            __hip_atomic_store(ws.ready + (int64_t)t.g * S + s, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __syncthreads();
+    if (publish_and_count<LAYOUT>(v, t, j, s, K, S, k, cg, rs, ws, streamed, sh)) {
+        reduce_strip<LAYOUT>(x, t, K, k, cg, rs, ws, scales, true, timeout_ticks, sh, cs);
         if (streamed) return;                             // the deferred kernel writes this group
-        cs = make_col_scales(*(const float4*)(sh_scale + cg * 8), *(const float4*)(sh_scale + cg * 8 + 4));
     } else {
         if (streamed) return;
-        // wait for the strip's scales, bounded in wall-clock time
-        if (threadIdx.x == 0) {
-            const uint32_t* rdy = ws.ready + (int64_t)t.g * S + s;
-            const unsigned long long t0 = wall_clock64();
-            int ok = 0;
-            while (true) {
-                if (__hip_atomic_load(rdy, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
-                    ok = 1;
-                    break;
+        // wait for the strip's scales: the rs == 0 lanes poll their 8 columns
+        // (bounded in wall-clock time) and pass them on through LDS
+        int ok = 1;
+        if (rs == 0 && k < K) {
+            const float* sp = scales + (int64_t)t.g * K + k;
+            uint4 s0 = load_coherent(sp), s1 = load_coherent(sp + 4);
+            if (!scales_written(s0, s1)) {
+                const unsigned long long t0 = wall_clock64();
+                while (true) {
+                    __builtin_amdgcn_s_sleep(2);
+                    s0 = load_coherent(sp);
+                    s1 = load_coherent(sp + 4);
+                    if (scales_written(s0, s1)) break;
+                    if (wall_clock64() - t0 > timeout_ticks) {
+                        ok = 0;
+                        break;
+                    }
                 }
-                if (wall_clock64() - t0 > timeout_ticks) break;
-                __builtin_amdgcn_s_sleep(2);
             }
-            if (!ok && deferred_launched) {
-                __hip_atomic_store(ws.deferred + (int64_t)j * S + s, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(ws.any, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-            order_acquire();
-            sh_state = ok ? 2 : deferred_launched ? 3 : 4;
+            *(float4*)(sh.scale + cg * 8) = bits_f4(s0);
+            *(float4*)(sh.scale + cg * 8 + 4) = bits_f4(s1);
         }
-        __syncthreads();
-        if (sh_state == 3) return;                        // left for the deferred kernel
-        if (sh_state == 4) {
+        if (__syncthreads_or(!ok)) {
+            if (deferred_launched) {
+                // left for the deferred kernel, which runs after every strip is reduced
+                if (threadIdx.x == 0) {
+                    __hip_atomic_store(ws.deferred + (int64_t)j * S + s, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_store(ws.any, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+                return;
+            }
             // The wait ran out and no deferred pass follows: reduce this strip's
             // maxima over all of the group's rows straight from the input (slow,
             // only when the device cannot keep the group's tiles resident).
-            uint4 a = make_uint4(0, 0, 0, 0);
-            if (k < K)
-                for (int r = t.gr0 + rs; r < t.gr1; r += C::NS) max8(a, abs8(*(const uint4*)(x + (int64_t)r * K + k)));
-            red[rs][cg] = a;
+            uint4 a = strip_max_from_x(x, K, t, k, rs, C::NS);
+            sh.red[rs][cg] = a;
             __syncthreads();
             if (rs == 0) {
 #pragma unroll
-                for (int r = 1; r < C::NS; ++r) max8(a, red[r][cg]);
-                *(float4*)(sh_scale + cg * 8) = scales_lo(a);
-                *(float4*)(sh_scale + cg * 8 + 4) = scales_hi(a);
+                for (int r = 1; r < C::NS; ++r) max8(a, sh.red[r][cg]);
+                *(float4*)(sh.scale + cg * 8) = scales_lo(a);
+                *(float4*)(sh.scale + cg * 8 + 4) = scales_hi(a);
             }
             __syncthreads();
-            cs = make_col_scales(*(const float4*)(sh_scale + cg * 8), *(const float4*)(sh_scale + cg * 8 + 4));
-        } else if (k < K) {
-            cs = make_col_scales(bits_f4(load_coherent(scales + (int64_t)t.g * K + k)),
-                                 bits_f4(load_coherent(scales + (int64_t)t.g * K + k + 4)));
+        }
+        cs = make_col_scales(*(const float4*)(sh.scale + cg * 8), *(const float4*)(sh.scale + cg * 8 + 4));
+    }
+    quantize_store_tile<LAYOUT>(v, cs, t, M, K, k, cg, rs, q, sh.stage, false);
+}
+
+// ------------------------------------------------------------ two-pass ----
+// The alternative to holding: an amax pass (every tile publishes its column
+// maxima and counts itself in; the last tile of a (group, strip) reduces them
+// into the scales; nobody waits), then a quantize pass that reads X again.
+// 5 bytes moved per element instead of 3, but no workgroup ever waits for
+// another, so both passes stream at full speed.
+template <int LAYOUT>
+__global__ __launch_bounds__(kTThreads)
+void group_amax_kernel(const uint16_t* __restrict__ x, int K, int G, int S, int SB, int slots, Workspace ws,
+                       float* __restrict__ scales, unsigned long long timeout_ticks)
+{
+    using C = TileCfg<LAYOUT>;
+    __shared__ TileShared<LAYOUT, false> sh;
+    int j, s;
+    tile_of_block((int)blockIdx.x, slots, SB, j, s);
+    write_empty_group_scales(G, K, ws, scales, kTThreads);
+    const TileInfo t = tile_info<C::R>(ws.table, j, s);
+    if (t.g < 0 || t.g == G) return;                      // unused chunk id or rows past the last end (uniform)
+    const int cg = (int)threadIdx.x % C::CG, rs = (int)threadIdx.x / C::CG;
+    const int k = s * C::W + cg * 8;
+    uint4 v[kHold];
+    load_tile<LAYOUT>(x, K, t, k, rs, v);
+    if (publish_and_count<LAYOUT>(v, t, j, s, K, S, k, cg, rs, ws, false, sh)) {
+        ColScales cs;
+        reduce_strip<LAYOUT>(x, t, K, k, cg, rs, ws, scales, false, timeout_ticks, sh, cs);
+    }
+}
+
+template <int LAYOUT>
+__global__ __launch_bounds__(kTThreads)
+void group_quant_kernel(const uint16_t* __restrict__ x, int M, int K, int G, int S, Workspace ws,
+                        const float* __restrict__ scales, uint8_t* __restrict__ q)
+{
+    using C = TileCfg<LAYOUT>;
+    __shared__ __align__(16) uint8_t stage[LAYOUT == 1 ? C::W * C::R : 16];
+    const int j = (int)blockIdx.x / S, s = (int)blockIdx.x % S;
+    const TileInfo t = tile_info<C::R>(ws.table, j, s);
+    if (t.g < 0) return;                                  // unused chunk id (uniform)
+    const int cg = (int)threadIdx.x % C::CG, rs = (int)threadIdx.x / C::CG;
+    const int k = s * C::W + cg * 8;
+    ColScales cs;
+    uint4 v[kHold];
+    if (t.g < G) {
+        load_tile<LAYOUT>(x, K, t, k, rs, v);
+        if (k < K)
+            cs = make_col_scales(*(const float4*)(scales + (int64_t)t.g * K + k),
+                                 *(const float4*)(scales + (int64_t)t.g * K + k + 4));
+    }
+    quantize_store_tile<LAYOUT>(v, cs, t, M, K, k, cg, rs, q, stage, t.g == G);
+}
+
+// Column-major quantize pass over 128-row blocks that ignore group boundaries,
+// so every output row (a column of X) gets whole 128-byte lines, never a
+// partial line shared with the neighbouring group's tile.  Each row takes its
+// own group's scales: a lane walks its 16 consecutive rows, moving to the next
+// group (and loading its 8 scales) whenever a row reaches the group's end.
+// Rows are quantized row-wise (8 codes per row) and the lane's 16 x 8 code
+// block is transposed in registers (byte permutes) into 8 columns of 16 rows.
+__device__ __forceinline__ void transpose4x4_bytes(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3, uint32_t out[4])
+{
+    // w_r holds columns 0..3 of row r; out[c] holds rows 0..3 of column c
+    const uint32_t t01_lo = __builtin_amdgcn_perm(w1, w0, 0x05010400u);   // w0.0 w1.0 w0.1 w1.1
+    const uint32_t t01_hi = __builtin_amdgcn_perm(w1, w0, 0x07030602u);   // w0.2 w1.2 w0.3 w1.3
+    const uint32_t t23_lo = __builtin_amdgcn_perm(w3, w2, 0x05010400u);
+    const uint32_t t23_hi = __builtin_amdgcn_perm(w3, w2, 0x07030602u);
+    out[0] = __builtin_amdgcn_perm(t23_lo, t01_lo, 0x05040100u);
+    out[1] = __builtin_amdgcn_perm(t23_lo, t01_lo, 0x07060302u);
+    out[2] = __builtin_amdgcn_perm(t23_hi, t01_hi, 0x05040100u);
+    out[3] = __builtin_amdgcn_perm(t23_hi, t01_hi, 0x07060302u);
+}
+
+__global__ __launch_bounds__(kTThreads)
+void group_quant_col_blocks_kernel(const uint16_t* __restrict__ x, int M, int K, int G, int S, Workspace ws,
+                                   const float* __restrict__ scales, uint8_t* __restrict__ q)
+{
+    using C = TileCfg<1>;
+    __shared__ __align__(16) uint8_t stage[C::W * C::R];
+    const int blk = (int)blockIdx.x / S, s = (int)blockIdx.x % S;
+    const int a = blk * C::R;
+    const int cg = (int)threadIdx.x % C::CG, rs = (int)threadIdx.x / C::CG;
+    const int k = s * C::W + cg * 8;
+    TileInfo t;
+    t.a = a;
+    t.r0 = a;
+    t.r1 = a + C::R < M ? a + C::R : M;
+    t.s = s;
+    uint4 v[kHold];
+    load_tile<1>(x, K, t, k, rs, v);
+
+    // codes of this lane's 16 rows, row by row, each with its group's scales
+    const int row0 = a + rs * kHold;
+    int g = ws.bfirst[blk];
+    int gend = g < G ? ws.gend[g] : 0x7FFFFFFF;
+    ColScales cs;
+    bool have = false;
+    uint2 out[kHold];
+#pragma unroll
+    for (int i = 0; i < kHold; ++i) {
+        const int row = row0 + i;
+        if (row >= gend) {
+            do {
+                ++g;
+                gend = g < G ? ws.gend[g] : 0x7FFFFFFF;
+            } while (row >= gend);
+            have = false;
+        }
+        if (!have && g < G && k < K) {
+            cs = make_col_scales(*(const float4*)(scales + (int64_t)g * K + k),
+                                 *(const float4*)(scales + (int64_t)g * K + k + 4));
+            have = true;
+        }
+        // rows past the last end, and past M, get code 0 (the latter are not stored)
+        out[i] = (g < G && row < M) ? group_quantize_chunk(v[i], cs) : make_uint2(0, 0);
+    }
+    // 16 rows x 8 columns of codes -> 8 columns x 16 rows in the staging tile
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {           // columns 0..3, then 4..7
+        uint32_t col[4][4];                          // [column][row quad]
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+            uint32_t o4[4];
+            transpose4x4_bytes(half ? out[4 * qd].y : out[4 * qd].x, half ? out[4 * qd + 1].y : out[4 * qd + 1].x,
+                               half ? out[4 * qd + 2].y : out[4 * qd + 2].x, half ? out[4 * qd + 3].y : out[4 * qd + 3].x,
+                               o4);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) col[c][qd] = o4[c];
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            *(uint4*)(stage + col_tile_offset(cg * 8 + half * 4 + c, rs * kHold)) =
+                make_uint4(col[c][0], col[c][1], col[c][2], col[c][3]);
+    }
+    __syncthreads();
+    // column cc of the block becomes output row (strip * W + cc): rows [0, r1 - a)
+    const int hi = t.r1 - a;
+    const bool aligned16 = (M & 15) == 0;
+    const int64_t col0 = (int64_t)s * C::W;
+    for (int it = 0; it < (C::W * 8) / kTThreads; ++it) {
+        const int sid = (int)threadIdx.x + kTThreads * it;
+        const int cc = sid >> 3, seg = sid & 7;
+        if (col0 + cc >= K) continue;
+        const int rb = seg * 16;
+        if (rb >= hi) continue;
+        const uint4 val = *(const uint4*)(stage + col_tile_offset(cc, rb));
+        uint8_t* dst = q + (col0 + cc) * (int64_t)M + a + rb;
+        if (aligned16 && rb + 16 <= hi) {
+            *(uint4*)dst = val;
+        } else {
+            store_partial16(val, dst, 0, rb + 16 < hi ? 16 : hi - rb, aligned16);
         }
     }
-    quantize_store_tile<LAYOUT>(v, cs, t, M, K, k, cg, rs, q, stage, false);
 }
 
 // ------------------------------------------------------------ deferred ----
@@ -658,16 +942,18 @@ static hipError_t launch_layout(const void* x, int M, int K, const int32_t* offs
                                 void* workspace, hipStream_t stream)
 {
     using C = TileCfg<LAYOUT>;
-    size_t off[6];
+    size_t off[8];
     workspace_layout<LAYOUT>(M, K, G, off);
     uint8_t* base = (uint8_t*)workspace;
     Workspace ws;
     ws.table = (ChunkEntry*)(base + off[0]);
     ws.partial = (uint16_t*)(base + off[1]);
     ws.count = (uint32_t*)(base + off[2]);
-    ws.ready = (uint32_t*)(base + off[3]);
+    ws.empty = (uint32_t*)(base + off[3]);
     ws.deferred = (uint32_t*)(base + off[4]);
     ws.any = (uint32_t*)(base + off[5]);
+    ws.gend = (int32_t*)(base + off[6]);
+    ws.bfirst = (int32_t*)(base + off[7]);
     const int S = (K + C::W - 1) / C::W;
     const int64_t slots = chunk_slots(M, C::R, G);
     const int nGS = G * S;
@@ -696,10 +982,34 @@ static hipError_t launch_layout(const void* x, int M, int K, const int32_t* offs
     if (wait_us < 0) wait_us = 0;
     const unsigned long long timeout_ticks =
         (unsigned long long)(rate_khz > 0 ? rate_khz : 100000) * (unsigned long long)wait_us / 1000ull;
+    // MXQ_GROUP_MODE=hold|twopass picks the method (default: the faster one measured
+    // for the layout).
+    bool twopass = LAYOUT == 1;
+    if (const char* v = getenv("MXQ_GROUP_MODE")) {
+        if (strcmp(v, "twopass") == 0) twopass = true;
+        if (strcmp(v, "hold") == 0) twopass = false;
+    }
 
-    hipLaunchKernelGGL(group_plan_kernel<C::R>, dim3(64), dim3(kGThreads), 0, stream, offs, G, M, K, ws, nGS,
-                       (int)nTiles, (int)slots, scales);
-    if (M > 0) {
+    // the fills are a few MB: give them enough blocks (the scales are polled
+    // only by the hold kernel)
+    const int nPartial16 = (int)(slots * K / 8);
+    const int nScale16 = M > 0 && !twopass ? (int)((int64_t)G * K / 4) : 0;
+    int pgrid = (int)(((int64_t)nPartial16 + nScale16) / (kGThreads * 8));
+    pgrid = pgrid < 64 ? 64 : pgrid > 1024 ? 1024 : pgrid;
+    hipLaunchKernelGGL(group_plan_kernel<C::R>, dim3(pgrid), dim3(kGThreads), 0, stream, offs, G, M, K, ws, nGS,
+                       (int)nTiles, (int)slots, scales, nPartial16, nScale16);
+    if (M > 0 && twopass) {
+        hipLaunchKernelGGL(group_amax_kernel<LAYOUT>, dim3((unsigned)nTiles), dim3(kTThreads), 0, stream,
+                           (const uint16_t*)x, K, G, S, 1, (int)slots, ws, scales, timeout_ticks);
+        if (LAYOUT == 1) {
+            const int nBlk = (M + C::R - 1) / C::R;
+            hipLaunchKernelGGL(group_quant_col_blocks_kernel, dim3((unsigned)(nBlk * S)), dim3(kTThreads), 0, stream,
+                               (const uint16_t*)x, M, K, G, S, ws, (const float*)scales, (uint8_t*)q);
+        } else {
+            hipLaunchKernelGGL(group_quant_kernel<LAYOUT>, dim3((unsigned)nTiles), dim3(kTThreads), 0, stream,
+                               (const uint16_t*)x, M, K, G, S, ws, (const float*)scales, (uint8_t*)q);
+        }
+    } else if (M > 0) {
         // No group spans more than ceil(M/R) + 1 chunks: unless that exceeds the
         // hold limit nothing is streamed, and tiles whose wait runs out finish
         // themselves, so the deferred pass is not launched at all.
