@@ -106,6 +106,7 @@ struct Workspace {
     uint32_t* count;      // [G][S] arrivals per (group, strip)
     uint32_t* empty;      // [G] 1 if the group has no rows
     int32_t* gend;        // [G] end row of each group (offsets clamped as documented)
+    int32_t* gchunks;     // [G][2] first chunk id and chunk count of each group
     int32_t* bfirst;      // [ceil(M/128)] group containing the first row of each 128-row block (G: none)
     uint32_t* deferred;   // [slots][S] 1 if the tile was left for the deferred kernel
     uint32_t* any;        // [1] 1 if any tile needs the deferred kernel
@@ -116,7 +117,7 @@ static size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 static int64_t chunk_slots(int64_t M, int R, int64_t G) { return (M + R - 1) / R + G + 1; }
 
 template <int LAYOUT>
-static size_t workspace_layout(int64_t M, int64_t K, int64_t G, size_t off[8])
+static size_t workspace_layout(int64_t M, int64_t K, int64_t G, size_t off[9])
 {
     using C = TileCfg<LAYOUT>;
     const int64_t slots = chunk_slots(M, C::R, G);
@@ -130,6 +131,7 @@ static size_t workspace_layout(int64_t M, int64_t K, int64_t G, size_t off[8])
     off[5] = o; o += 256;
     off[6] = o; o += align256((size_t)(G * 4));
     off[7] = o; o += align256((size_t)(((M + 127) / 128 + 1) * 4));
+    off[8] = o; o += align256((size_t)(G * 8));
     return o;
 }
 
@@ -147,7 +149,7 @@ bool group_scale_sizes_ok(int64_t M, int64_t K, int64_t G)
 
 size_t group_scale_workspace_bytes(int64_t M, int64_t K, int32_t G)
 {
-    size_t off[8];
+    size_t off[9];
     const size_t a = workspace_layout<0>(M, K, G, off);
     const size_t b = workspace_layout<1>(M, K, G, off);
     return a > b ? a : b;
@@ -448,6 +450,8 @@ void group_plan_kernel(const int32_t* __restrict__ offs, int G, int M, int K, Wo
             if (g < G) {
                 ws.empty[g] = e <= st ? 1u : 0u;
                 ws.gend[g] = e;
+                ws.gchunks[2 * g] = incl - cnt;
+                ws.gchunks[2 * g + 1] = cnt;
             }
             // 128-row blocks whose first row is in this group (or past the last end)
             if (g <= G)
@@ -753,30 +757,70 @@ void group_hold_kernel(const uint16_t* __restrict__ x, int M, int K, int G, int 
 }
 
 // ------------------------------------------------------------ two-pass ----
-// The alternative to holding: an amax pass (every tile publishes its column
-// maxima and counts itself in; the last tile of a (group, strip) reduces them
-// into the scales; nobody waits), then a quantize pass that reads X again.
-// 5 bytes moved per element instead of 3, but no workgroup ever waits for
-// another, so both passes stream at full speed.
+// The alternative to holding: an amax pass (every tile stores its column maxima
+// as one partial row), a finalize pass (one workgroup per (group, strip)
+// reduces the group's partial rows and divides), then a quantize pass that
+// reads X again.  5 bytes moved per element instead of 3, but no workgroup ever
+// waits for another, so every pass streams.
+// Amax pass: one workgroup per tile (the hold kernel's tiles); its column
+// maxima become the tile's piece of the chunk's partial row.
 template <int LAYOUT>
 __global__ __launch_bounds__(kTThreads)
-void group_amax_kernel(const uint16_t* __restrict__ x, int K, int G, int S, int SB, int slots, Workspace ws,
-                       float* __restrict__ scales, unsigned long long timeout_ticks)
+void group_amax_kernel(const uint16_t* __restrict__ x, int K, int G, int S, Workspace ws)
 {
     using C = TileCfg<LAYOUT>;
-    __shared__ TileShared<LAYOUT, false> sh;
-    int j, s;
-    tile_of_block((int)blockIdx.x, slots, SB, j, s);
-    write_empty_group_scales(G, K, ws, scales, kTThreads);
+    __shared__ uint4 red[C::NS][C::CG];
+    const int j = (int)blockIdx.x / S, s = (int)blockIdx.x % S;
     const TileInfo t = tile_info<C::R>(ws.table, j, s);
     if (t.g < 0 || t.g == G) return;                      // unused chunk id or rows past the last end (uniform)
     const int cg = (int)threadIdx.x % C::CG, rs = (int)threadIdx.x / C::CG;
     const int k = s * C::W + cg * 8;
     uint4 v[kHold];
     load_tile<LAYOUT>(x, K, t, k, rs, v);
-    if (publish_and_count<LAYOUT>(v, t, j, s, K, S, k, cg, rs, ws, false, sh)) {
-        ColScales cs;
-        reduce_strip<LAYOUT>(x, t, K, k, cg, rs, ws, scales, false, timeout_ticks, sh, cs);
+    uint4 m = abs8(v[0]);
+#pragma unroll
+    for (int i = 1; i < kHold; ++i) max8(m, abs8(v[i]));
+    red[rs][cg] = m;
+    __syncthreads();
+    if (rs == 0 && k < K) {
+#pragma unroll
+        for (int r = 1; r < C::NS; ++r) max8(m, red[r][cg]);
+        *(uint4*)(ws.partial + (int64_t)j * K + k) = m;
+    }
+}
+
+// One workgroup per (group, strip of 128 columns): lane (cg, rs) reduces
+// partial rows rs, rs + 16, ... of the group for columns 8cg..8cg+7.  An empty
+// group (no chunks) gets the scale of amax 0.
+constexpr int kFThreads = 256, kFW = 128, kFCG = kFW / 8, kFNS = kFThreads / kFCG;
+__global__ __launch_bounds__(kFThreads)
+void group_finalize_kernel(int K, int SF, Workspace ws, float* __restrict__ scales)
+{
+    __shared__ uint4 red[kFNS][kFCG];
+    const int g = (int)blockIdx.x / SF, s = (int)blockIdx.x % SF;
+    const int first = ws.gchunks[2 * g], count = ws.gchunks[2 * g + 1];
+    const int cg = (int)threadIdx.x % kFCG, rs = (int)threadIdx.x / kFCG;
+    const int k = s * kFW + cg * 8;
+    uint4 a = make_uint4(0, 0, 0, 0);
+    if (k < K) {
+        const uint16_t* p = ws.partial + (int64_t)first * K + k;
+        int c = rs;
+        for (; c + 3 * kFNS < count; c += 4 * kFNS) {
+            uint4 b[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) b[u] = *(const uint4*)(p + (int64_t)(c + u * kFNS) * K);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) max8(a, b[u]);
+        }
+        for (; c < count; c += kFNS) max8(a, *(const uint4*)(p + (int64_t)c * K));
+    }
+    red[rs][cg] = a;
+    __syncthreads();
+    if (rs == 0 && k < K) {
+#pragma unroll
+        for (int r = 1; r < kFNS; ++r) max8(a, red[r][cg]);
+        *(float4*)(scales + (int64_t)g * K + k) = scales_lo(a);
+        *(float4*)(scales + (int64_t)g * K + k + 4) = scales_hi(a);
     }
 }
 
@@ -942,7 +986,7 @@ static hipError_t launch_layout(const void* x, int M, int K, const int32_t* offs
                                 void* workspace, hipStream_t stream)
 {
     using C = TileCfg<LAYOUT>;
-    size_t off[8];
+    size_t off[9];
     workspace_layout<LAYOUT>(M, K, G, off);
     uint8_t* base = (uint8_t*)workspace;
     Workspace ws;
@@ -954,6 +998,7 @@ static hipError_t launch_layout(const void* x, int M, int K, const int32_t* offs
     ws.any = (uint32_t*)(base + off[5]);
     ws.gend = (int32_t*)(base + off[6]);
     ws.bfirst = (int32_t*)(base + off[7]);
+    ws.gchunks = (int32_t*)(base + off[8]);
     const int S = (K + C::W - 1) / C::W;
     const int64_t slots = chunk_slots(M, C::R, G);
     const int nGS = G * S;
@@ -982,9 +1027,11 @@ static hipError_t launch_layout(const void* x, int M, int K, const int32_t* offs
     if (wait_us < 0) wait_us = 0;
     const unsigned long long timeout_ticks =
         (unsigned long long)(rate_khz > 0 ? rate_khz : 100000) * (unsigned long long)wait_us / 1000ull;
-    // MXQ_GROUP_MODE=hold|twopass picks the method (default: the faster one measured
-    // for the layout).
-    bool twopass = LAYOUT == 1;
+    // MXQ_GROUP_MODE=hold|twopass picks the method.  Default: hold, except for
+    // column-major output with many groups, where the hold kernel's tiles cut at
+    // group boundaries split too many output lines (measured crossover at about
+    // one group per two 128-row blocks).
+    bool twopass = LAYOUT == 1 && 2 * (int64_t)G >= (M + 127) / 128;
     if (const char* v = getenv("MXQ_GROUP_MODE")) {
         if (strcmp(v, "twopass") == 0) twopass = true;
         if (strcmp(v, "hold") == 0) twopass = false;
@@ -992,7 +1039,7 @@ static hipError_t launch_layout(const void* x, int M, int K, const int32_t* offs
 
     // the fills are a few MB: give them enough blocks (the scales are polled
     // only by the hold kernel)
-    const int nPartial16 = (int)(slots * K / 8);
+    const int nPartial16 = twopass ? 0 : (int)(slots * K / 8);   // (every partial row is written before it is read)
     const int nScale16 = M > 0 && !twopass ? (int)((int64_t)G * K / 4) : 0;
     int pgrid = (int)(((int64_t)nPartial16 + nScale16) / (kGThreads * 8));
     pgrid = pgrid < 64 ? 64 : pgrid > 1024 ? 1024 : pgrid;
@@ -1000,7 +1047,10 @@ static hipError_t launch_layout(const void* x, int M, int K, const int32_t* offs
                        (int)nTiles, (int)slots, scales, nPartial16, nScale16);
     if (M > 0 && twopass) {
         hipLaunchKernelGGL(group_amax_kernel<LAYOUT>, dim3((unsigned)nTiles), dim3(kTThreads), 0, stream,
-                           (const uint16_t*)x, K, G, S, 1, (int)slots, ws, scales, timeout_ticks);
+                           (const uint16_t*)x, K, G, S, ws);
+        const int SF = (K + kFW - 1) / kFW;
+        hipLaunchKernelGGL(group_finalize_kernel, dim3((unsigned)(G * SF)), dim3(kFThreads), 0, stream, K, SF, ws,
+                           scales);
         if (LAYOUT == 1) {
             const int nBlk = (M + C::R - 1) / C::R;
             hipLaunchKernelGGL(group_quant_col_blocks_kernel, dim3((unsigned)(nBlk * S)), dim3(kTThreads), 0, stream,

@@ -90,8 +90,13 @@ EDGE_CASES = {
 }
 
 
+MODES = ["hold", "twopass"]
+
+
+@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("case", list(EDGE_CASES), ids=list(EDGE_CASES))
-def test_edge_cases(case):
+def test_edge_cases(case, mode, monkeypatch):
+    monkeypatch.setenv("MXQ_GROUP_MODE", mode)
     M, K, sizes = EDGE_CASES[case]
     rng = np.random.default_rng(len(case) * 1000 + M)
     if sizes is None:
@@ -103,7 +108,9 @@ def test_edge_cases(case):
     check_group(x_bits, ends, name=case)
 
 
-def test_out_of_contract_offsets_are_clamped():
+@pytest.mark.parametrize("mode", MODES)
+def test_out_of_contract_offsets_are_clamped(mode, monkeypatch):
+    monkeypatch.setenv("MXQ_GROUP_MODE", mode)
     M, K = 300, 64
     rng = np.random.default_rng(21)
     x_bits = (rng.standard_normal((M, K)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
@@ -111,7 +118,9 @@ def test_out_of_contract_offsets_are_clamped():
         check_group(x_bits, np.array(ends, np.int32), name=f"ends {ends}")
 
 
-def test_nonfinite_columns():
+@pytest.mark.parametrize("mode", MODES)
+def test_nonfinite_columns(mode, monkeypatch):
+    monkeypatch.setenv("MXQ_GROUP_MODE", mode)
     M, K = 260, 48
     rng = np.random.default_rng(22)
     x_bits = (rng.standard_normal((M, K)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
@@ -139,10 +148,12 @@ def tokens_bits():
     return W.bf16_bits(W.moe_tokens())
 
 
-def test_tokens_g16_row_full_size(tokens_bits):
-    """(16640, 5120), 16 Zipf(1.1) groups, row-major output: every byte."""
+@pytest.mark.parametrize("mode", MODES)
+def test_tokens_g16_full_size(tokens_bits, mode, monkeypatch):
+    """(16640, 5120), 16 Zipf(1.1) groups, both layouts, both methods: every byte."""
+    monkeypatch.setenv("MXQ_GROUP_MODE", mode)
     ends = W.zipf_group_ends(W.TOKENS_SHAPE[0], 16)
-    check_group(tokens_bits, ends, layouts=(ROW,), name="G=16")
+    check_group(tokens_bits, ends, name=f"G=16 {mode}")
 
 
 @pytest.mark.parametrize("G", [32, 64, 128])
@@ -181,19 +192,24 @@ def test_transpose_shapes(R, C):
     assert og.guard_intact()
 
 
-# The hold kernel keeps each tile on chip until its group's scales are known;
+# The hold method keeps each tile on chip until its group's scales are known;
 # groups too large to hold, and tiles whose bounded wait runs out, go through
-# the deferred kernel.  Force both routes from the host and check the bytes.
+# the deferred kernel.  The two-pass method's last arrivals poll partial rows
+# (bounded too).  Force every route from the host and check the bytes.
+HOLD = {"MXQ_GROUP_MODE": "hold"}
 ROUTES = {
-    "held": {},
-    "all_streamed": {"MXQ_GROUP_HOLD_TILES": "0"},
+    "held": {**HOLD},
+    "all_streamed": {**HOLD, "MXQ_GROUP_HOLD_TILES": "0"},
     # no deferred pass is launched for these sizes: timed-out tiles finish themselves
-    "all_waits_time_out": {"MXQ_GROUP_WAIT_US": "0"},
+    "all_waits_time_out": {**HOLD, "MXQ_GROUP_WAIT_US": "0"},
     # groups of more than 5 chunks streamed, smaller ones held
-    "small_hold_limit": {"MXQ_GROUP_HOLD_TILES": "5"},
+    "small_hold_limit": {**HOLD, "MXQ_GROUP_HOLD_TILES": "5"},
     # deferred pass launched and every waiting tile defers to it
-    "time_outs_deferred": {"MXQ_GROUP_HOLD_TILES": "5", "MXQ_GROUP_WAIT_US": "0"},
-    "launch_order_strip_fastest": {"MXQ_GROUP_STRIP_BLOCK": "2"},
+    "time_outs_deferred": {**HOLD, "MXQ_GROUP_HOLD_TILES": "5", "MXQ_GROUP_WAIT_US": "0"},
+    "launch_order_strip_fastest": {**HOLD, "MXQ_GROUP_STRIP_BLOCK": "2"},
+    "twopass": {"MXQ_GROUP_MODE": "twopass"},
+    # a partial row not yet visible to the last arrival: reduce from the input
+    "twopass_waits_time_out": {"MXQ_GROUP_MODE": "twopass", "MXQ_GROUP_WAIT_US": "0"},
 }
 
 
