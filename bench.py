@@ -71,7 +71,7 @@ def parse_args():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-mx-rows", type=int, default=16384, help="dispatch rows in the CPU sample")
     p.add_argument("--cpu-group-rows", type=int, default=8320, help="token rows in the CPU sample")
-    p.add_argument("--ingest-counters", nargs=3, metavar=("STATS_CSV", "FETCH_CSV", "WRITE_CSV"),
+    p.add_argument("--ingest-counters", nargs="+", metavar="CSV",
                    help="turn rocprofv3 outputs of this script (kernel stats, FETCH_SIZE and WRITE_SIZE "
                         "counter collections) into the summaries under profiles/ and exit")
     p.add_argument("--profile-commands", default="", help="text recorded with --ingest-counters")
@@ -83,10 +83,11 @@ COPY_KERNEL = "__amd_rocclr_copyBuffer"
 COPY_BYTES = 1 << 30       # the 1 GiB device copies of the streaming-ceiling leg
 
 
-def ingest_counters(stats_csv, fetch_csv, write_csv, commands):
+def ingest_counters(stats_csv, fetch_csv, write_csv, sq_csv=None, commands=""):
     """Summaries for profiles/: per-kernel durations (kernel-trace stats) and
     HBM bytes per dispatch from FETCH_SIZE / WRITE_SIZE (KiB), each scaled by what
-    the counter reads for the 1 GiB copies of known size."""
+    the counter reads for the 1 GiB copies of known size; optionally vector
+    memory / LDS instruction counts and LDS bank conflicts per dispatch."""
     import csv
     import collections
     import statistics
@@ -102,7 +103,8 @@ def ingest_counters(stats_csv, fetch_csv, write_csv, commands):
     w_copy = max(write[COPY_KERNEL]) * 1024.0
     f_scale, w_scale = COPY_BYTES / f_copy, COPY_BYTES / w_copy
     stats = {r["Name"].split("(")[0]: r for r in csv.DictReader(open(stats_csv))}
-    algo = {"mxq::mx_quantize_kernel": mx_bytes(*DISPATCH), "mxq::mx_dequantize_kernel": mx_bytes(*DISPATCH)}
+    algo = {"mxq::mx_quantize_kernel": mx_bytes(*DISPATCH), "mxq::mx_dequantize_kernel": mx_bytes(*DISPATCH),
+            "mxq::transpose_u8_kernel": transpose_bytes(*TOKENS)}
     lines = ["# HBM traffic per dispatch, hot-path step (dispatch payload 65536x5120, tokens 16640x5120)", "",
              "Commands (from the repository root):", "", "```", commands.strip(), "```", "",
              f"Calibration: {COPY_KERNEL} copies of 1 GiB read {f_copy / 1024:.1f} KiB by FETCH_SIZE and "
@@ -123,6 +125,36 @@ def ingest_counters(stats_csv, fetch_csv, write_csv, commands):
         if a:
             out["kernels"][k.split("::")[-1]] = {"hbm_bytes_per_launch": round(hbm), "algorithmic_bytes": a,
                                                  "source_sha256": src_hash}
+    # whole group-scaling calls: the kernels each call launches (the plan kernel
+    # is shared by both calls and counted once per call)
+    def per_dispatch(k):
+        if k not in fetch or k not in write:
+            return None
+        return statistics.mean(fetch[k]) * 1024 * f_scale + statistics.mean(write[k]) * 1024 * w_scale
+    calls = [("group scaling G=16 row-major (plan + hold)", ["void mxq::group_plan_kernel<128>", "void mxq::group_hold_kernel<0>"],
+              group_bytes(TOKENS[0], TOKENS[1], 16)),
+             ("group scaling G=128 column-major (plan + amax + finalize + quantize)",
+              ["void mxq::group_plan_kernel<128>", "void mxq::group_amax_kernel<1>", "mxq::group_finalize_kernel",
+               "mxq::group_quant_col_blocks_kernel"], group_bytes(TOKENS[0], TOKENS[1], 128))]
+    lines += ["", "Whole calls (sum of the kernels each call launches):", "",
+              "| call | scaled HBM bytes | algorithmic bytes | ratio |", "|---|---|---|---|"]
+    for name, ks, a in calls:
+        parts = [per_dispatch(k) for k in ks]
+        if any(x is None for x in parts):
+            continue
+        lines.append(f"| {name} | {sum(parts):,.0f} | {a} | {sum(parts) / a:.4f} |")
+    if sq_csv:
+        sq = collections.defaultdict(lambda: collections.defaultdict(list))
+        for r in csv.DictReader(open(sq_csv)):
+            sq[r["Kernel_Name"].split("(")[0]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+        names = sorted({c for k in sq.values() for c in k})
+        lines += ["", "Vector memory, LDS and wave counts per dispatch (means):", "",
+                  "| kernel | " + " | ".join(names) + " |", "|---" * (len(names) + 1) + "|"]
+        for k in sorted(sq):
+            if k == COPY_KERNEL:
+                continue
+            lines.append(f"| {k} | " + " | ".join(f"{statistics.mean(sq[k][c]):,.0f}" if sq[k][c] else "-"
+                                                 for c in names) + " |")
     lines += ["", "Kernel durations (rocprofv3 --kernel-trace --stats):", "",
               "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
     for k, r in stats.items():
@@ -156,7 +188,9 @@ def cpu_info():
 def main():
     args = parse_args()
     if args.ingest_counters:
-        ingest_counters(*args.ingest_counters, args.profile_commands)
+        if len(args.ingest_counters) not in (3, 4):
+            raise SystemExit("--ingest-counters STATS_CSV FETCH_CSV WRITE_CSV [SQ_CSV]")
+        ingest_counters(*args.ingest_counters, commands=args.profile_commands)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
