@@ -66,6 +66,8 @@ _SIGS = {
     "oracle_e4m3_encode_f32_array": (None, [_P, _i64, _P]),
     "oracle_bf16_round_f64_array": (None, [_P, _i64, _P]),
     "oracle_group_encode_elements": (None, [_P, _P, _i64, _P]),
+    "oracle_mx_grouped_mm": (None, [_P, _P, _P, _P, _P, _i64, _i64, _i64, _i32,
+                                    _P, _i64, _P, _i64, _P]),
 }
 
 
@@ -168,6 +170,36 @@ class Oracle:
         if R and C:
             self._L.oracle_transpose_u8(_ptr(a), R, C, _ptr(out))
         return out
+
+    def mx_grouped_mm(self, xq, xs, wq, ws, group_end, rows=None, cols=None):
+        """Y[rows][:, cols] of the grouped product of MXFP8 operands, float64.
+
+        xq (M, K) / xs (M, K/32): tokens; wq (G, N, K) / ws (G, N, K/32): one
+        weight per group; Y[m, n] = sum_k x(m, k) w_g(n, k) for m in group g,
+        0 for rows past the last (clamped) end.  rows / cols default to all."""
+        xq = np.ascontiguousarray(xq, dtype=np.uint8)
+        xs = np.ascontiguousarray(xs, dtype=np.uint8)
+        wq = np.ascontiguousarray(wq, dtype=np.uint8)
+        ws = np.ascontiguousarray(ws, dtype=np.uint8)
+        M, K = xq.shape
+        G, N, Kw = wq.shape
+        if Kw != K or K % 32 or xs.shape != (M, K // 32) or ws.shape != (G, N, K // 32):
+            raise ValueError("operand shapes do not match")
+        ends = np.ascontiguousarray(np.asarray(group_end, dtype=np.int32))
+        if ends.shape != (G,):
+            raise ValueError("need one end offset per group")
+        rows = np.arange(M, dtype=np.int64) if rows is None else np.ascontiguousarray(rows, np.int64)
+        cols = np.arange(N, dtype=np.int64) if cols is None else np.ascontiguousarray(cols, np.int64)
+        if rows.size and (rows.min() < 0 or rows.max() >= M):
+            raise ValueError("row index out of range")
+        if cols.size and (cols.min() < 0 or cols.max() >= N):
+            raise ValueError("column index out of range")
+        y = np.zeros((rows.size, cols.size), np.float64)
+        if rows.size and cols.size:
+            self._L.oracle_mx_grouped_mm(_ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), _ptr(ends),
+                                         M, N, K, G, _ptr(rows), rows.size, _ptr(cols),
+                                         cols.size, _ptr(y))
+        return y
 
     # ----------------------------------------------- element-wise arrays --
     def mx_encode_elements(self, x_bits, scale_codes):

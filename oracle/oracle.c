@@ -16,7 +16,9 @@
  *   [GRP]  "[moe training] fix uncoalesced global accesses in per group rowwise
  *          scaling kernel" (torchao PR 2761), Summary: per-group float8 scaling
  *          whose output feeds the LHS of a scaled grouped GEMM, written row-major
- *          or column-major (then transformed).
+ *          or column-major (then transformed).  The grouped product itself
+ *          (token rows of group g times the transpose of expert g's weight, both
+ *          as MXFP8) is the MoE GEMM configuration built on these operands.
  *   MXFP8 itself is the OCP Microscaling (MX) v1.0 format that the name refers
  *   to: blocks of 32 elements share one E8M0 power-of-two scale whose exponent
  *   is floor(log2(amax)) minus the element format's largest exponent (8 for
@@ -34,7 +36,10 @@
  *     the fp32 multiplier s is the stored scale; a column with Inf/NaN gets
  *     s = NaN and payload 0x7F; group g spans rows [end(g-1), end(g)) with the
  *     end offsets clamped to be non-decreasing and <= M; rows past the last end
- *     get 0x00.
+ *     get 0x00;
+ *   - grouped product: operands are MXFP8 along K (the contraction dimension);
+ *     the reference value is the double-precision sum of the exactly
+ *     dequantized products; rows past the last end give 0.
  *
  * Build: gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math -fPIC -shared
  * (x86-64 SSE arithmetic: binary32 ops are correctly rounded, no x87 excess
@@ -293,6 +298,64 @@ void oracle_transpose_u8(const uint8_t* in, int64_t R, int64_t C, uint8_t* out)
     for (int64_t i = 0; i < R; ++i)
         for (int64_t j = 0; j < C; ++j)
             out[j * R + i] = in[i * C + j];
+}
+
+/* ----------------------------------------------- scaled grouped GEMM --- */
+
+/* Grouped product of MXFP8 operands, in double.
+ * [GRP] Summary (the group-scaled tokens are the LHS of a scaled grouped GEMM)
+ * and the MoE configuration "Y_g = X_g W_g^T": token rows of group g are
+ * multiplied by the transpose of expert g's weight.
+ *   xq (M, K) E4M3 and xs (M, K/32) E8M0: the tokens, MX blocks along K.
+ *   wq (G, N, K) E4M3 and ws (G, N, K/32) E8M0: one (N, K) weight per group.
+ *   group_end: G cumulative ends, clamped as in oracle_group_scale.
+ * Computes y[i, j] = Y[rows[i], cols[j]] for the requested rows and columns:
+ * the sum over k of x(r, k) * w_g(n, k), where each operand value is its E4M3
+ * code times its block's E8M0 scale (exact in double, as is every product),
+ * accumulated in double in k order.  A row at or past the last end belongs to
+ * no group and gives 0.  The two 256-entry tables below only cache
+ * oracle_e4m3_decode / oracle_e8m0_decode. */
+void oracle_mx_grouped_mm(const uint8_t* xq, const uint8_t* xs,
+                          const uint8_t* wq, const uint8_t* ws,
+                          const int32_t* group_end, int64_t M, int64_t N, int64_t K,
+                          int32_t G, const int64_t* rows, int64_t nrows,
+                          const int64_t* cols, int64_t ncols, double* y)
+{
+    double e4m3[256], e8m0[256];
+    for (int c = 0; c < 256; ++c) {
+        e4m3[c] = oracle_e4m3_decode((uint8_t)c);
+        e8m0[c] = oracle_e8m0_decode((uint8_t)c);
+    }
+    const int64_t KB = K / 32;
+    for (int64_t i = 0; i < nrows; ++i) {
+        int64_t r = rows[i];
+        /* group of row r under the clamped ends */
+        int32_t grp = -1;
+        int64_t start = 0;
+        for (int32_t g = 0; g < G; ++g) {
+            int64_t end = group_end[g];
+            end = end < start ? start : end;     /* running maximum */
+            end = end > M ? M : end;
+            if (r >= start && r < end) { grp = g; break; }
+            start = end;
+        }
+        for (int64_t j = 0; j < ncols; ++j) {
+            int64_t n = cols[j];
+            double acc = 0.0;
+            if (grp >= 0) {
+                const uint8_t* wrow = wq + ((int64_t)grp * N + n) * K;
+                const uint8_t* wsrow = ws + ((int64_t)grp * N + n) * KB;
+                const uint8_t* xrow = xq + r * K;
+                const uint8_t* xsrow = xs + r * KB;
+                for (int64_t k = 0; k < K; ++k) {
+                    double xv = e4m3[xrow[k]] * e8m0[xsrow[k / 32]];
+                    double wv = e4m3[wrow[k]] * e8m0[wsrow[k / 32]];
+                    acc += xv * wv;
+                }
+            }
+            y[i * ncols + j] = acc;
+        }
+    }
 }
 
 /* ------------------------------------------- element-wise array forms ----- */

@@ -14,6 +14,8 @@ Kinds of pin used here:
     grid midpoint (exact in binary64), over all bf16 patterns x all scale codes;
   * closed facts of the formats (code counts, extreme codes);
   * hand-worked fixtures in tests/golden/;
+  * torch float64 matmuls of operands dequantized by torch's decoders (the
+    grouped product), and closed forms of constant operands;
   * invariants: exact dequantization for scale codes >= 3, idempotence,
     the per-block maximum landing in [256, 448], slicing and permutation
     invariance of group scaling, the two layouts being transposes.
@@ -346,12 +348,129 @@ def check_transpose(o, seed=13):
         assert np.array_equal(o.transpose_u8(t), a)
 
 
+# ------------------------------------------------ scaled grouped GEMM ---
+def _random_mx_operand(rng, shape, scale_lo=112, scale_hi=142):
+    """Random finite E4M3 codes (never 0x7F / 0xFF) and E8M0 codes in a range."""
+    q = rng.integers(0, 256, size=shape).astype(np.uint8)
+    q[(q & 0x7F) == 0x7F] ^= 0x01
+    s = rng.integers(scale_lo, scale_hi, size=shape[:-1] + (shape[-1] // 32,)).astype(np.uint8)
+    return q, s
+
+
+def mx_values_by_torch(q, s):
+    """Dequantized MXFP8 values from torch's own E4M3 and E8M0 decoders, float64."""
+    v = torch.from_numpy(np.ascontiguousarray(q)).view(torch.float8_e4m3fn).to(torch.float64)
+    sc = torch.from_numpy(np.ascontiguousarray(s)).view(torch.float8_e8m0fnu).to(torch.float64)
+    return (v * sc.repeat_interleave(32, dim=-1)).numpy()
+
+
+def grouped_mm_by_torch(xq, xs, wq, ws, ends):
+    """Y (M, N) float64 from torch matmuls of torch-dequantized operands, and the
+    matching sum of |products| (the scale of the rounding in any summation order)."""
+    X = mx_values_by_torch(xq, xs)
+    W = mx_values_by_torch(wq, ws)
+    M = X.shape[0]
+    N = W.shape[1]
+    Y = np.zeros((M, N))
+    A = np.zeros((M, N))
+    start = 0
+    for g, e in enumerate(ends):
+        end = min(max(int(e), start), M)
+        Xg = torch.from_numpy(X[start:end])
+        Wg = torch.from_numpy(W[g])
+        Y[start:end] = (Xg @ Wg.T).numpy()
+        A[start:end] = (Xg.abs() @ Wg.abs().T).numpy()
+        start = end
+    return Y, A
+
+
+def check_grouped_mm_vs_torch(o, seed=14):
+    """Ragged groups (one empty, one cut tail row range) against torch's decoders
+    and float64 matmul; only the summation order differs."""
+    rng = np.random.default_rng(seed)
+    M, N, K = 150, 40, 192
+    for ends in ([40, 40, 97, 130], [150], [0, 10, 150, 150]):
+        G = len(ends)
+        xq, xs = _random_mx_operand(rng, (M, K))
+        wq, ws = _random_mx_operand(rng, (G, N, K))
+        y = o.mx_grouped_mm(xq, xs, wq, ws, ends)
+        ref, mag = grouped_mm_by_torch(xq, xs, wq, ws, ends)
+        assert y.shape == (M, N)
+        assert np.all(np.abs(y - ref) <= 1e-13 * mag), ends
+        # sampled rows and columns are the same numbers
+        rows = np.array([0, 39, 40, 96, 97, 129, 130, 149])
+        cols = np.array([0, 7, 39])
+        assert np.array_equal(o.mx_grouped_mm(xq, xs, wq, ws, ends, rows, cols), y[np.ix_(rows, cols)])
+
+
+def check_grouped_mm_closed_form(o):
+    """All operand values 1 with weight scale 2^g: Y = K * 2^g on group g's rows,
+    0 past the last end; decreasing ends act as their running maximum."""
+    M, N, K, G = 30, 8, 96, 4
+    xq = np.full((M, K), 0x38, np.uint8)          # E4M3 1.0
+    xs = np.full((M, K // 32), 127, np.uint8)     # 2^0
+    wq = np.full((G, N, K), 0x38, np.uint8)
+    ws = np.empty((G, N, K // 32), np.uint8)
+    for g in range(G):
+        ws[g] = 127 + g
+    y = o.mx_grouped_mm(xq, xs, wq, ws, [6, 2, 11, 25])     # -> [6, 6, 11, 25]
+    expect = np.zeros((M, N))
+    expect[0:6] = K * 1.0
+    expect[6:11] = K * 4.0
+    expect[11:25] = K * 8.0
+    assert np.array_equal(y, expect)
+    # one E4M3 code in one weight row changes exactly that output column's sum
+    wq2 = wq.copy()
+    wq2[3, 5, 70] = 0xC0                          # -2.0 instead of 1.0
+    y2 = o.mx_grouped_mm(xq, xs, wq2, ws, [6, 2, 11, 25])
+    expect[11:25, 5] -= 3.0 * 8.0
+    assert np.array_equal(y2, expect)
+
+
+def check_grouped_mm_block_scales(o):
+    """Each E8M0 scale covers its own 32 consecutive k: doubling one block's
+    scale adds exactly that block's partial sum."""
+    rng = np.random.default_rng(15)
+    M, N, K = 6, 5, 128
+    xq, xs = _random_mx_operand(rng, (M, K), 120, 130)
+    wq, ws = _random_mx_operand(rng, (1, N, K), 120, 130)
+    y = o.mx_grouped_mm(xq, xs, wq, ws, [M])
+    X = mx_values_by_torch(xq, xs)
+    W = mx_values_by_torch(wq, ws)[0]
+    for b in range(K // 32):
+        xs2 = xs.copy()
+        xs2[2, b] += 1
+        y2 = o.mx_grouped_mm(xq, xs2, wq, ws, [M])
+        part = X[2, 32 * b:32 * b + 32] @ W[:, 32 * b:32 * b + 32].T
+        mag = np.abs(X[2]) @ np.abs(W).T
+        assert np.all(np.abs(y2[2] - (y[2] + part)) <= 1e-13 * 2 * mag)
+        assert np.array_equal(np.delete(y2, 2, 0), np.delete(y, 2, 0))
+
+
+def check_grouped_mm_nan(o):
+    """A NaN scale code (0xFF) or a NaN E4M3 code poisons exactly the outputs it
+    enters."""
+    M, N, K = 4, 3, 64
+    xq = np.full((M, K), 0x38, np.uint8)
+    xs = np.full((M, K // 32), 127, np.uint8)
+    wq = np.full((1, N, K), 0x38, np.uint8)
+    ws = np.full((1, N, K // 32), 127, np.uint8)
+    ws[0, 1, 1] = 0xFF
+    xq[2, 5] = 0x7F
+    y = o.mx_grouped_mm(xq, xs, wq, ws, [M])
+    nan = np.isnan(y)
+    assert nan[:, 1].all() and nan[2, :].all()
+    assert nan.sum() == M + N - 1
+
+
 FAST_CHECKS = [
     check_e4m3_decode_vs_torch, check_e4m3_code_facts, check_e4m3_encode_roundtrip,
     check_e8m0_decode_vs_torch, check_bf16_round_vs_torch, check_e4m3_encode_vs_torch_saturating,
     check_mx_worked_blocks, check_mx_invariants, check_mx_row_block_layout,
     check_group_worked, check_group_vs_libraries, check_group_invariants,
     check_group_offsets_clamped, check_transpose,
+    check_grouped_mm_vs_torch, check_grouped_mm_closed_form, check_grouped_mm_block_scales,
+    check_grouped_mm_nan,
 ]
 
 

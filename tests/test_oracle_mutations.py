@@ -31,6 +31,14 @@ MUTATIONS = [
     ("group_col_layout_wrong", "else q[k * M + r] = c;", "else q[r * K + k] = c;"),
     ("group_start_not_advanced", "        start = end;\n    }", "    }"),
     ("group_decreasing_end_kept", "if (end < start) end = start;", ""),
+    ("mm_block_scale_index", "e8m0[wsrow[k / 32]]", "e8m0[wsrow[k % KB]]"),
+    ("mm_token_scale_row", "const uint8_t* xsrow = xs + r * KB;", "const uint8_t* xsrow = xs + (r / 2) * KB;"),
+    ("mm_weight_group_ignored", "wq + ((int64_t)grp * N + n) * K;", "wq + ((int64_t)0 * N + n) * K;"),
+    ("mm_weight_uses_token_scale", "double wv = e4m3[wrow[k]] * e8m0[wsrow[k / 32]];",
+     "double wv = e4m3[wrow[k]] * e8m0[xsrow[k / 32]];"),
+    ("mm_tail_rows_in_group0", "int32_t grp = -1;", "int32_t grp = 0;"),
+    ("mm_group_end_inclusive", "if (r >= start && r < end) { grp = g; break; }",
+     "if (r >= start && r <= end) { grp = g; break; }"),
     ("transpose_identity", "out[j * R + i] = in[i * C + j];", "out[i * C + j] = in[i * C + j];"),
 ]
 

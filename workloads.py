@@ -20,6 +20,9 @@ per group rowwise scaling kernel", Performance tables):
   routing    16640 tokens drawn to G experts with probabilities proportional
              to (g + 1) ** -1.1 (Zipf 1.1, expert 0 hottest); group g's size is
              the count of tokens drawn to it; end offsets are the running sums.
+  experts    W (16, 8192, 5120): one (N, K) weight per expert, N(0, 0.02^2) --
+             the right operand of the grouped product Y_g = X_g W_g^T over the
+             tokens routed to expert g.
 """
 from __future__ import annotations
 
@@ -30,6 +33,8 @@ TINY_SHAPE = (512, 256)
 TINY_GROUP_SIZES = (100, 37, 0, 375)
 DISPATCH_SHAPE = (65536, 5120)
 TOKENS_SHAPE = (16640, 5120)
+EXPERTS_SHAPE = (16, 8192, 5120)
+EXPERT_WEIGHT_STD = 0.02
 ZIPF_ALPHA = 1.1
 
 
@@ -112,3 +117,11 @@ def random_bf16_bits(shape, seed: int, finite_only: bool = True) -> np.ndarray:
         bad = (bits & 0x7F80) == 0x7F80
         bits[bad] &= 0xBFFF  # clear the top exponent bit: now finite
     return bits
+
+
+def expert_weights(G: int = EXPERTS_SHAPE[0], N: int = EXPERTS_SHAPE[1], K: int = EXPERTS_SHAPE[2],
+                   seed: int = 2) -> torch.Tensor:
+    """(G, N, K) bf16 expert weights ~ N(0, 0.02^2), drawn in fp32 and cast once."""
+    w = torch.randn((G, N, K), generator=_gen(seed), dtype=torch.float32)
+    w.mul_(EXPERT_WEIGHT_STD)
+    return w.to(torch.bfloat16)
