@@ -47,6 +47,7 @@ const char* mxq_status_string(int status)
     case MXQ_ERR_WORKSPACE: return "MXQ_ERR_WORKSPACE: workspace missing or too small";
     case MXQ_ERR_HIP: return "MXQ_ERR_HIP: a HIP runtime call failed";
     case MXQ_ERR_NOT_IMPLEMENTED: return "MXQ_ERR_NOT_IMPLEMENTED";
+    case MXQ_ERR_DTYPE: return "MXQ_ERR_DTYPE: unknown output data type";
     default: return "unknown mxq_status";
     }
 }
@@ -125,6 +126,41 @@ mxq_status mxq_transpose_u8(const void* in, int64_t R, int64_t C, void* out, voi
     if (!in || !out) return MXQ_ERR_NULL;
     if (!aligned16(in) || !aligned16(out)) return MXQ_ERR_ALIGN;
     return hip_status(mxq::launch_transpose_u8(in, R, C, out, (hipStream_t)stream));
+}
+
+static mxq_status check_grouped_mm_sizes(int64_t M, int64_t N, int64_t K, int64_t G)
+{
+    if (M < 0 || N < 0 || K <= 0) return MXQ_ERR_SHAPE;
+    if (!mxq::grouped_mm_sizes_ok(M, N, K, G)) return MXQ_ERR_SHAPE;
+    return MXQ_OK;
+}
+
+size_t mxq_grouped_mm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t G)
+{
+    if (check_grouped_mm_sizes(M, N, K, G) != MXQ_OK) return 0;
+    return mxq::grouped_mm_workspace_bytes(M, N, G);
+}
+
+mxq_status mxq_scaled_grouped_mm(const void* xq_e4m3, const void* xs_e8m0, const void* wq_e4m3,
+                                 const void* ws_e8m0, const int32_t* group_end_offs, int64_t M,
+                                 int64_t N, int64_t K, int32_t G, int out_dtype, void* y,
+                                 void* workspace, size_t workspace_bytes, void* stream)
+{
+    mxq_status st = check_grouped_mm_sizes(M, N, K, G);
+    if (st != MXQ_OK) return st;
+    if (out_dtype != MXQ_OUT_BF16 && out_dtype != MXQ_OUT_F32) return MXQ_ERR_DTYPE;
+    if (M == 0 || N == 0) return MXQ_OK;
+    if (!xq_e4m3 || !xs_e8m0 || !wq_e4m3 || !ws_e8m0 || !group_end_offs || !y) return MXQ_ERR_NULL;
+    if (!aligned16(xq_e4m3) || !aligned16(xs_e8m0) || !aligned16(wq_e4m3) || !aligned16(ws_e8m0) ||
+        !aligned16(y))
+        return MXQ_ERR_ALIGN;
+    if (((uintptr_t)group_end_offs & 3u) != 0) return MXQ_ERR_ALIGN;
+    const size_t need = mxq::grouped_mm_workspace_bytes(M, N, G);
+    if (!workspace || workspace_bytes < need) return MXQ_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return MXQ_ERR_ALIGN;
+    return hip_status(mxq::launch_grouped_mm(xq_e4m3, xs_e8m0, wq_e4m3, ws_e8m0, group_end_offs, (int)M, (int)N,
+                                             (int)K, (int)G, y, out_dtype == MXQ_OUT_F32, workspace,
+                                             (hipStream_t)stream));
 }
 
 }  // extern "C"

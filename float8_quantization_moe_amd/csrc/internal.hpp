@@ -16,6 +16,13 @@ size_t group_scale_workspace_bytes(int64_t M, int64_t K, int32_t G);
 hipError_t launch_group_scale(const void* x, int M, int K, const int32_t* offs, int G, int layout,
                               void* q, float* scales, void* workspace, hipStream_t stream);
 
+int grouped_mm_max_groups();
+bool grouped_mm_sizes_ok(int64_t M, int64_t N, int64_t K, int64_t G);
+size_t grouped_mm_workspace_bytes(int64_t M, int64_t N, int32_t G);
+hipError_t launch_grouped_mm(const void* xq, const void* xs, const void* wq, const void* ws,
+                             const int32_t* offs, int M, int N, int K, int G, void* y, bool f32_out,
+                             void* workspace, hipStream_t stream);
+
 hipError_t launch_transpose_u8(const void* in, int64_t R, int64_t C, void* out, hipStream_t stream);
 
 }  // namespace mxq

@@ -7,9 +7,10 @@ is no fallback: if the library is missing or a call fails, an exception is
 raised.
 
 Sources of the operations: "[mxfp8 MoE training] Support mxfp8 all to all in
-expert parallel" (Summary) for the MXFP8 codec, and "[moe training] fix
+expert parallel" (Summary) for the MXFP8 codec, "[moe training] fix
 uncoalesced global accesses in per group rowwise scaling kernel" (Summary) for
-the group scaling and the layout transform.
+the group scaling and the layout transform, and "[float8] add float8 rowwise
+MoE prototype" (Summary) for the scaled grouped GEMM.
 """
 from __future__ import annotations
 
@@ -25,10 +26,13 @@ MXQ_LAYOUT_ROW = 0
 MXQ_LAYOUT_COL = 1
 MXQ_OK = 0
 MXQ_ERR_NULL, MXQ_ERR_SHAPE, MXQ_ERR_ALIGN, MXQ_ERR_LAYOUT, MXQ_ERR_WORKSPACE, MXQ_ERR_HIP = 1, 2, 3, 4, 5, 6
+MXQ_ERR_DTYPE = 8
+MXQ_OUT_BF16 = 0
+MXQ_OUT_F32 = 1
 
 EXPORTED = ("mxq_abi_version", "mxq_status_string", "mxq_last_hip_error", "mxq_quantize_mx",
             "mxq_dequantize_mx", "mxq_group_scale_workspace_bytes", "mxq_group_scale_fp8",
-            "mxq_transpose_u8")
+            "mxq_transpose_u8", "mxq_grouped_mm_workspace_bytes", "mxq_scaled_grouped_mm")
 
 
 class MxqError(RuntimeError):
@@ -68,6 +72,10 @@ def lib() -> ctypes.CDLL:
         L.mxq_group_scale_fp8.argtypes = [P, i64, i64, P, i32, ctypes.c_int, P, P, P, sz, P]
         L.mxq_transpose_u8.restype = ctypes.c_int
         L.mxq_transpose_u8.argtypes = [P, i64, i64, P, P]
+        L.mxq_grouped_mm_workspace_bytes.restype = sz
+        L.mxq_grouped_mm_workspace_bytes.argtypes = [i64, i64, i64, i32]
+        L.mxq_scaled_grouped_mm.restype = ctypes.c_int
+        L.mxq_scaled_grouped_mm.argtypes = [P, P, P, P, P, i64, i64, i64, i32, ctypes.c_int, P, P, sz, P]
         _lib = L
     return _lib
 
@@ -158,6 +166,42 @@ def mxq_transpose_u8(inp: torch.Tensor, out: torch.Tensor, stream=None) -> None:
     _check(lib().mxq_transpose_u8(pi, R, C, po, _stream(stream)), "mxq_transpose_u8")
 
 
+def mxq_grouped_mm_workspace_bytes(M: int, N: int, K: int, G: int) -> int:
+    return int(lib().mxq_grouped_mm_workspace_bytes(int(M), int(N), int(K), int(G)))
+
+
+def mxq_scaled_grouped_mm(xq: torch.Tensor, xs: torch.Tensor, wq: torch.Tensor, ws: torch.Tensor,
+                          group_end_offs: torch.Tensor, y: torch.Tensor, workspace: torch.Tensor,
+                          stream=None) -> None:
+    """xq (M, K) / xs (M, K/32) and wq (G, N, K) / ws (G, N, K/32) uint8 MXFP8
+    operands, group_end_offs int32[G] (device) -> y (M, N) bf16 or float32."""
+    if xq.dim() != 2 or wq.dim() != 3 or y.dim() != 2:
+        raise ValueError("xq must be (M, K), wq (G, N, K) and y (M, N)")
+    M, K = xq.shape
+    G, N, Kw = wq.shape
+    if Kw != K or tuple(y.shape) != (M, N):
+        raise ValueError("operand shapes do not match")
+    if group_end_offs.numel() != G:
+        raise ValueError("need one end offset per group")
+    if y.dtype == torch.bfloat16:
+        out_dtype = MXQ_OUT_BF16
+    elif y.dtype == torch.float32:
+        out_dtype = MXQ_OUT_F32
+    else:
+        raise TypeError("y must be bfloat16 or float32")
+    kb = K // 32 if K % 32 == 0 else None
+    pxq = _dev(xq, "xq", torch.uint8)
+    pxs = _dev(xs, "xs", torch.uint8, M * kb if kb is not None else None)
+    pwq = _dev(wq, "wq", torch.uint8)
+    pws = _dev(ws, "ws", torch.uint8, G * N * kb if kb is not None else None)
+    po = _dev(group_end_offs, "group_end_offs", torch.int32)
+    py = _dev(y, "y")
+    pw = _dev(workspace, "workspace")
+    wbytes = workspace.numel() * workspace.element_size()
+    _check(lib().mxq_scaled_grouped_mm(pxq, pxs, pwq, pws, po, M, N, K, G, out_dtype, py, pw, wbytes,
+                                       _stream(stream)), "mxq_scaled_grouped_mm")
+
+
 # ---------------------------------------------------------------- helpers ---
 # Allocate outputs with torch and call the entry points above.
 
@@ -191,3 +235,14 @@ def transpose_u8(inp: torch.Tensor, stream=None) -> torch.Tensor:
     out = torch.empty((C, R), dtype=torch.uint8, device=inp.device)
     mxq_transpose_u8(inp, out, stream)
     return out
+
+
+def scaled_grouped_mm(xq: torch.Tensor, xs: torch.Tensor, wq: torch.Tensor, ws: torch.Tensor,
+                      group_end_offs: torch.Tensor, out_dtype=torch.bfloat16, stream=None) -> torch.Tensor:
+    M, K = xq.shape
+    G, N, _ = wq.shape
+    y = torch.empty((M, N), dtype=out_dtype, device=xq.device)
+    wsp = torch.empty(max(mxq_grouped_mm_workspace_bytes(M, N, K, G), 16), dtype=torch.uint8,
+                      device=xq.device)
+    mxq_scaled_grouped_mm(xq, xs, wq, ws, group_end_offs, y, wsp, stream)
+    return y

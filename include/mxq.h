@@ -58,7 +58,8 @@ typedef enum mxq_status {
     MXQ_ERR_LAYOUT = 4,      /* unknown mxq_layout value                            */
     MXQ_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required          */
     MXQ_ERR_HIP = 6,         /* a HIP runtime call failed (launch, device query)    */
-    MXQ_ERR_NOT_IMPLEMENTED = 7
+    MXQ_ERR_NOT_IMPLEMENTED = 7,
+    MXQ_ERR_DTYPE = 8        /* unknown mxq_out_dtype value                         */
 } mxq_status;
 
 typedef enum mxq_layout {
@@ -67,6 +68,11 @@ typedef enum mxq_layout {
                                 (K, M) row-major operand of a GEMM that contracts
                                 over the tokens of each group                        */
 } mxq_layout;
+
+typedef enum mxq_out_dtype {
+    MXQ_OUT_BF16 = 0,        /* bfloat16, rounded to nearest even from the fp32 sum  */
+    MXQ_OUT_F32 = 1          /* the fp32 sum itself                                  */
+} mxq_out_dtype;
 
 /* MXQ_ABI_VERSION of the built library. */
 int mxq_abi_version(void);
@@ -172,6 +178,56 @@ mxq_status mxq_group_scale_fp8(const void* x_bf16, int64_t M, int64_t K,
  * overlap.
  */
 mxq_status mxq_transpose_u8(const void* in, int64_t R, int64_t C, void* out, void* stream);
+
+/*
+ * Bytes of device workspace mxq_scaled_grouped_mm needs for these sizes (0 for
+ * invalid sizes).  It holds the call's tile list, built on the device from the
+ * group offsets; contents need no initialisation, are meaningless after the
+ * call, and two calls in flight at once must not share it.
+ */
+size_t mxq_grouped_mm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t G);
+
+/*
+ * Grouped product of MXFP8 operands: Y[m, :] = X[m, :] W_g^T for every token row
+ * m of group g.
+ * Sources: "[float8] add float8 rowwise MoE prototype" (torchtitan PR 1245),
+ * Summary (the routed experts' grouped_mm becomes dynamic quantization plus a
+ * scaled grouped GEMM); "[mxfp8 MoE training] Support mxfp8 all to all in expert
+ * parallel", Performance table (MXFP8 for the grouped GEMMs); "[moe training]
+ * fix uncoalesced global accesses in per group rowwise scaling kernel", Summary
+ * (the group-ordered token tensor is the GEMM's left operand).
+ *
+ *   xq_e4m3 (M, K) uint8   token E4M3 codes, row-major;
+ *   xs_e8m0 (M, K/32) uint8 their E8M0 block scales (block b of row m covers
+ *           k = 32b .. 32b+31) -- exactly what mxq_quantize_mx writes for X;
+ *   wq_e4m3 (G, N, K) uint8 expert weights' E4M3 codes, W_g = wq[g] is (N, K)
+ *           row-major (the layout of an nn.Linear weight: K contiguous);
+ *   ws_e8m0 (G, N, K/32) uint8 their E8M0 block scales (mxq_quantize_mx of the
+ *           (G*N, K) weight);
+ *   group_end_offs DEVICE int32[G]: cumulative end offsets of the token groups,
+ *           clamped exactly as in mxq_group_scale_fp8 (running maximum, cut to
+ *           [0, M]); read on the device only;
+ *   out_dtype MXQ_OUT_BF16 or MXQ_OUT_F32;
+ *   y       (M, N) output, row-major, bf16 or fp32.  Rows at or past the last
+ *           clamped end belong to no group and are written as zeros.
+ *   workspace DEVICE scratch of mxq_grouped_mm_workspace_bytes(M, N, K, G) bytes.
+ *
+ * Arithmetic: each operand value is its E4M3 code times its block's power-of-two
+ * scale; the hardware forms the exact products, sums them in fp32 (blocks of 64
+ * k at a time) and the result is rounded once to the output type.  Against the
+ * exact sum of the same products the fp32 error is a few units in the last place
+ * of sum_k |x w|.  Codes 0x7F / 0xFF (E4M3 NaN) and scale 0xFF (E8M0 NaN) are
+ * outside the contract: the result of a row/column that meets one is
+ * unspecified (mxq_quantize_mx emits them only for blocks holding Inf or NaN).
+ *
+ * Requires K > 0 and K % 128 == 0, N % 8 == 0, 0 <= M < 2^31, 0 <= N < 2^31,
+ * K <= 2^23, 1 <= G <= 4095 (MXQ_ERR_SHAPE otherwise); M == 0 or N == 0 is a
+ * no-op.  All buffers 16-byte aligned except group_end_offs (4-byte).
+ */
+mxq_status mxq_scaled_grouped_mm(const void* xq_e4m3, const void* xs_e8m0, const void* wq_e4m3,
+                                 const void* ws_e8m0, const int32_t* group_end_offs, int64_t M,
+                                 int64_t N, int64_t K, int32_t G, int out_dtype, void* y,
+                                 void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -150,3 +150,18 @@ def exhaustive_mx_codes():
     q = np.tile(np.arange(256, dtype=np.uint8), (256, 1))
     s = np.repeat(np.arange(256, dtype=np.uint8)[:, None], 8, axis=1)
     return q, s
+
+
+def oracle_mx_grouped_mm(xq, xs, wq, ws, ends, rows, cols) -> np.ndarray:
+    """The oracle's grouped product at the given rows and columns, row blocks in
+    parallel threads (rows are independent by definition)."""
+    rows = np.asarray(rows, dtype=np.int64)
+    y = np.empty((rows.size, len(cols)), np.float64)
+
+    def run(sl):
+        a, b = sl
+        y[a:b] = oracle.mx_grouped_mm(xq, xs, wq, ws, ends, rows[a:b], cols)
+
+    with ThreadPoolExecutor(THREADS) as ex:
+        list(ex.map(run, _row_slices(rows.size, THREADS * 2)))
+    return y

@@ -28,7 +28,8 @@ def L():
 def test_header_declares_the_entry_points():
     names = _declared()
     for n in ("mxq_quantize_mx", "mxq_dequantize_mx", "mxq_group_scale_fp8",
-              "mxq_group_scale_workspace_bytes", "mxq_transpose_u8", "mxq_abi_version"):
+              "mxq_group_scale_workspace_bytes", "mxq_transpose_u8", "mxq_abi_version",
+              "mxq_grouped_mm_workspace_bytes", "mxq_scaled_grouped_mm"):
         assert n in names
 
 
@@ -42,7 +43,7 @@ def test_every_declared_symbol_is_exported(L):
 
 def test_abi_version_and_status_strings(L):
     assert L.mxq_abi_version() == 1
-    for code in range(0, 8):
+    for code in range(0, 9):
         assert L.mxq_status_string(code).startswith(b"MXQ_")
     assert L.mxq_status_string(99) == b"unknown mxq_status"
     assert L.mxq_last_hip_error() == 0
@@ -108,6 +109,43 @@ def test_transpose_argument_errors(L):
     assert L.mxq_transpose_u8(A, 3, 4, 0, S) == 1
     assert L.mxq_transpose_u8(A + 1, 3, 4, A, S) == 3
     assert L.mxq_transpose_u8(0, 0, 4, 0, S) == 0
+
+
+def test_grouped_mm_argument_errors(L):
+    S = 0
+    M, N, K, G = 700, 264, 384, 5
+    ws = L.mxq_grouped_mm_workspace_bytes(M, N, K, G)
+    assert ws >= 16 + 16 * ((M + 255) // 256 + G + 1) * ((N + 255) // 256)
+    assert L.mxq_grouped_mm_workspace_bytes(M, N, 320, G) == 0        # K % 128
+    assert L.mxq_grouped_mm_workspace_bytes(M, N, 0, G) == 0          # K == 0
+    assert L.mxq_grouped_mm_workspace_bytes(M, 260, K, G) == 0        # N % 8
+    assert L.mxq_grouped_mm_workspace_bytes(M, N, K, 0) == 0          # G < 1
+    assert L.mxq_grouped_mm_workspace_bytes(M, N, K, 4096) == 0       # G > 4095
+    assert L.mxq_grouped_mm_workspace_bytes(M, N, K, 4095) > 0
+    assert L.mxq_grouped_mm_workspace_bytes(M, N, 1 << 24, G) == 0    # K too large
+    f = L.mxq_scaled_grouped_mm
+    args = lambda **kw: [kw.get(k, d) for k, d in (
+        ("xq", A), ("xs", A), ("wq", A), ("wsc", A), ("offs", A), ("M", M), ("N", N), ("K", K),
+        ("G", G), ("dt", 0), ("y", A), ("ws", A), ("wb", ws), ("s", S))]
+    assert f(*args(K=320)) == 2
+    assert f(*args(N=12)) == 2
+    assert f(*args(G=0)) == 2
+    assert f(*args(M=-1)) == 2
+    assert f(*args(dt=2)) == 8                                          # unknown output type
+    assert f(*args(xq=0)) == 1
+    assert f(*args(xs=0)) == 1
+    assert f(*args(wq=0)) == 1
+    assert f(*args(wsc=0)) == 1
+    assert f(*args(offs=0)) == 1
+    assert f(*args(y=0)) == 1
+    assert f(*args(xq=A + 8)) == 3
+    assert f(*args(wsc=A + 4)) == 3
+    assert f(*args(y=A + 8)) == 3
+    assert f(*args(offs=A + 2)) == 3
+    assert f(*args(ws=0)) == 5
+    assert f(*args(wb=ws - 1)) == 5
+    assert f(*args(M=0, xq=0, y=0)) == 0                                # empty: no-op
+    assert f(*args(N=0, wq=0, y=0)) == 0
 
 
 def test_binding_refuses_host_tensors():
