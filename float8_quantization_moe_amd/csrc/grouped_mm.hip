@@ -42,6 +42,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <utility>
+
 #include "device_common.hpp"
 #include "internal.hpp"
 
@@ -50,15 +52,13 @@ namespace {
 
 constexpr int kBM = 256;        // token rows per tile
 constexpr int kBN = 256;        // output columns per tile
-constexpr int kBK = 128;        // K bytes per LDS stage
+constexpr int kBK = 64;         // K bytes per LDS stage (one MFMA k-step)
+constexpr int kKStep = 128;     // K must be a multiple of this (a scale word covers 128 k)
 constexpr int kThreads = 256;
 constexpr int kCB = 4;          // column tiles per block of the tile order
 constexpr int kXcds = 8;
 constexpr int kPlanThreads = 1024;
 
-constexpr int kTileBytes = kBM * kBK;                   // 32 KB of codes per operand
-constexpr int kScaleBytes = (kBK / 32) * kBM;           // 1 KB of scales per operand
-constexpr int kStageBytes = 2 * kTileBytes + 2 * kScaleBytes;
 static_assert(kBM == kBN, "one row count serves both operand tiles");
 
 typedef int v8i __attribute__((ext_vector_type(8)));
@@ -182,63 +182,129 @@ __global__ __launch_bounds__(kPlanThreads) void mm_plan_kernel(const int32_t* __
 }
 
 // ------------------------------------------------------------ tile kernel ---
-// Physical 16-byte chunk of logical chunk c in LDS row r (rows of 128 bytes).
-__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r ^ (r >> 3)) & 7); }
+// K advances kBK = 64 bytes (one MFMA k-step) per stage.  Stages live in a
+// 4-deep LDS ring filled by buffer-load-to-LDS (the data never passes through
+// VGPRs), so three stages are in flight while one is multiplied.  Scales
+// travel in chunks of 16 bytes per row (16 k-blocks = 8 stages), fetched four
+// stages before their first use into a 2-slot ring: one 16-byte request per
+// row instead of one 4-byte request per row per stage pair, which matters
+// because the L1's outstanding-request budget, not bytes, bounds the feed.
+constexpr int kRing = 4;
+constexpr int kChunkStages = 8;                         // stages per scale chunk
+constexpr int kTileBytes = kBM * kBK;                   // 16 KB of codes per operand per stage
+constexpr int kChunkBytes = kBM * 16;                   // 4 KB of scales per operand per chunk
+constexpr int kDataBytes = kRing * 2 * kTileBytes;      // 128 KB
+constexpr int kDummyBytes = 4 * 1024;                   // sink for loads that carry nothing
+constexpr int kLdsBytes = kDataBytes + 2 * 2 * kChunkBytes + kDummyBytes;   // + 16 KB + 4 KB
+static_assert(kBK == 64 && kChunkStages * kBK == 512, "a scale chunk is 16 k-blocks of 32");
 
-// Byte offset, in a stage's scale area, of the scale of tile row r for k-block kb:
-// rows 128*h + 32*i + c (i = 0..3) of one k-block sit in one 32-bit word.
-__device__ __forceinline__ int scale_slot(int r, int kb)
+typedef __attribute__((address_space(3))) uint8_t* LdsPtr;
+typedef int v4i __attribute__((ext_vector_type(4)));
+constexpr uint32_t kOOB = 0xFFFFFFF0u;                  // past every buffer resource used here
+
+// Buffer resource in SGPRs for the asm loads below: base, stride 0, size in
+// bytes (loads at or past it return zeros), raw-buffer flags.
+__device__ __forceinline__ v4i make_srd(const void* base, uint32_t bytes)
 {
-    return kb * kBM + (r >> 7) * 128 + (r & 31) * 4 + ((r >> 5) & 3);
+    const uint64_t b = (uint64_t)(uintptr_t)base;
+    v4i r = {(int)(uint32_t)b, (int)(uint32_t)(b >> 32), (int)bytes, 0x00020000};
+    return r;
 }
 
-struct StageRegs {
-    uint4 a[8];                  // W_g codes
-    uint4 b[8];                  // X codes
-    uint32_t sa, sb;             // 4 scale bytes of one W_g row and one X row
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p)
+{
+    return (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)(LdsPtr)p);
+}
+
+// Buffer load straight into LDS: each lane's `bytes` bytes land at
+// lds + lane * bytes (M0 holds the wave-uniform LDS address).  The load has no
+// VGPR result; its completion is counted by vmcnt, which the stage barrier waits
+// on explicitly.  Written in asm so that the compiler does not add a
+// conservative wait for it before every later LDS read.  (M0 is reserved by the
+// compiler and set before each of its own uses; nothing else here reads it.)
+__device__ __forceinline__ void dma16(const v4i& srd, uint32_t lds, uint32_t voff)
+{
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds), "v"(voff), "s"(srd)
+                 : "memory");
+}
+__device__ __forceinline__ void dma4(const v4i& srd, uint32_t lds, uint32_t voff)
+{
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(lds), "v"(voff), "s"(srd)
+                 : "memory");
+}
+
+// Physical 16-byte chunk of logical chunk c in LDS row r (rows of 64 bytes).
+// The fragment reads (lane -> row c32 of a 32-row tile, chunks hk and 2 + hk)
+// measured conflict-free on gfx950 with this swizzle (4 LDS cycles per
+// 128-bit wave read); without it they take 4x as long.
+__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 2) & 3); }
+
+// Loads of stage t, per wave: 2 scale-chunk loads, then 8 data loads into
+// ring slot t % 4.  Stage 0 carries chunk 0 and stage 8c + 4 chunk c + 1 (if
+// that chunk starts before the last stage); other stages issue the 2 chunk
+// loads anyway, out of range and into a sink, and every stage up to the last
+// + 3 issues its 8 data loads (past the real K they read zeros into a slot
+// nobody reads).  So every stage is exactly 10 loads and no branch splits the
+// loop body.
+__device__ __forceinline__ int scale_chunk_of(int t, int nk)
+{
+    if (t == 0) return 0;
+    if ((t & 7) == 4 && t + 4 < nk) return (t + 4) >> 3;
+    return -1;
+}
+constexpr int kLoadsPerStage = 10;
+
+__device__ __forceinline__ void issue_chunk(int t, int nk, const v4i& wsr, const v4i& xsr, uint32_t KB,
+                                            uint8_t* lds, int wave, int lane)
+{
+    const int c = scale_chunk_of(t, nk);
+    const uint32_t real = lds_addr(lds + kDataBytes + (c & 1) * 2 * kChunkBytes + 64 * 16 * wave);
+    const uint32_t sink = lds_addr(lds + kDataBytes + 2 * 2 * kChunkBytes + 1024 * wave);
+    const uint32_t off = c >= 0 ? (uint32_t)(64 * wave + lane) * KB + (uint32_t)c * 16u : kOOB;
+    dma16(wsr, c >= 0 ? real : sink, off);
+    dma16(xsr, c >= 0 ? real + kChunkBytes : sink, off);
+}
+
+// Per-wave state of the data loads: the lane's offset of load i (rows
+// 64*wave + 16*i .. +15, its swizzled 16-byte chunk) and the LDS address of
+// the wave's first row in slot 0.
+struct DataLoads {
+    v4i wr, xr;
+    uint32_t off[4];
+    uint32_t lds0;
+    int nk;
 };
 
-__device__ __forceinline__ void load_stage(StageRegs& s, Rsrc wr, Rsrc xr, Rsrc wsr, Rsrc xsr, uint32_t K, int k0)
+// Data load k (0..7) of stage t: rows of load k/2 of A (k even) or B.
+template <int KL>
+__device__ __forceinline__ void issue_data(const DataLoads& d, int t)
 {
-    const int t = threadIdx.x;
-    const uint32_t chunk = (uint32_t)(t & 7) * 16u + (uint32_t)k0;
-#pragma unroll
-    for (int p = 0; p < 8; ++p) {
-        const uint32_t row = (uint32_t)((t >> 3) + 32 * p);
-        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(wr, row * K + chunk, 0, 0);
-        s.a[p] = make_uint4(v.x, v.y, v.z, v.w);
-    }
-#pragma unroll
-    for (int p = 0; p < 8; ++p) {
-        const uint32_t row = (uint32_t)((t >> 3) + 32 * p);
-        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(xr, row * K + chunk, 0, 0);
-        s.b[p] = make_uint4(v.x, v.y, v.z, v.w);
-    }
-    const uint32_t soff = (uint32_t)t * (K / 32u) + (uint32_t)(k0 / 32);
-    s.sa = __builtin_amdgcn_raw_buffer_load_b32(wsr, soff, 0, 0);
-    s.sb = __builtin_amdgcn_raw_buffer_load_b32(xsr, soff, 0, 0);
+    constexpr int i = KL >> 1, op = KL & 1;
+    const uint32_t dst = d.lds0 + (uint32_t)(t & (kRing - 1)) * 2 * kTileBytes + op * kTileBytes + 16 * i * kBK;
+    const uint32_t off = t < d.nk ? d.off[i] + (uint32_t)t * kBK : kOOB;
+    dma16(op == 0 ? d.wr : d.xr, dst, off);
 }
 
-__device__ __forceinline__ void store_stage(const StageRegs& s, uint8_t* stage)
+__device__ __forceinline__ void issue_stage(int t, int nk, const v4i& wsr, const v4i& xsr, uint32_t KB, uint8_t* lds,
+                                            int wave, int lane, const DataLoads& d)
 {
-    const int t = threadIdx.x;
-    uint8_t* A = stage;
-    uint8_t* B = stage + kTileBytes;
-    uint8_t* SA = stage + 2 * kTileBytes;
-    uint8_t* SB = SA + kScaleBytes;
-#pragma unroll
-    for (int p = 0; p < 8; ++p) {
-        const int row = (t >> 3) + 32 * p;
-        const int off = row * kBK + (swz(row, t & 7) << 4);
-        *reinterpret_cast<uint4*>(A + off) = s.a[p];
-        *reinterpret_cast<uint4*>(B + off) = s.b[p];
-    }
-#pragma unroll
-    for (int kb = 0; kb < kBK / 32; ++kb) {
-        SA[scale_slot(t, kb)] = (uint8_t)(s.sa >> (8 * kb));
-        SB[scale_slot(t, kb)] = (uint8_t)(s.sb >> (8 * kb));
-    }
+    issue_chunk(t, nk, wsr, xsr, KB, lds, wave, lane);
+    issue_data<0>(d, t); issue_data<1>(d, t); issue_data<2>(d, t); issue_data<3>(d, t);
+    issue_data<4>(d, t); issue_data<5>(d, t); issue_data<6>(d, t); issue_data<7>(d, t);
 }
+
+// Wait until at most N of this wave's buffer loads are outstanding and its LDS
+// reads are done, then meet the other waves.  (No memory fence: a fence would
+// also wait for the loads still meant to be in flight.)
+template <int N>
+__device__ __forceinline__ void stage_barrier()
+{
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// Top of stage s: its loads (and all older ones) done; stages s+1 and s+2 may
+// still be in flight.
+__device__ __forceinline__ void stage_wait() { stage_barrier<2 * kLoadsPerStage>(); }
 
 // One lane's MFMA operand: logical 16-byte chunks c0 and c1 of LDS row r.
 __device__ __forceinline__ v8i read_frag(const uint8_t* tile, int r, int c0, int c1)
@@ -250,37 +316,71 @@ __device__ __forceinline__ v8i read_frag(const uint8_t* tile, int r, int c0, int
 }
 
 // acc[tn][tm] += A-tile tn x B-tile tm for all 16 pairs.  Operands are E4M3
-// (format code 0 for both); op_sel picks byte tn of sa and byte tm of sb, the
-// E8M0 scales of the lane's row in those tiles.
-template <int TN, int TM>
-__device__ __forceinline__ void mma_tiles(v16f (&acc)[4][4], const v8i (&a)[4], const v8i (&b)[4], int sa, int sb)
+// (format code 0 for both); op_sel OPS picks the byte of sa[tn] / sb[tm] that
+// holds the E8M0 scale of the lane's row and k-block.
+template <int TN, int TM, int OPS>
+__device__ __forceinline__ void mma_tiles(v16f (&acc)[4][4], const v8i (&a)[4], const v8i (&b)[4], const int (&sa)[4],
+                                          const int (&sb)[4])
 {
-    acc[TN][TM] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[TN], b[TM], acc[TN][TM], 0, 0, TN, sa, TM, sb);
-    if constexpr (TM + 1 < 4) mma_tiles<TN, TM + 1>(acc, a, b, sa, sb);
-    else if constexpr (TN + 1 < 4) mma_tiles<TN + 1, 0>(acc, a, b, sa, sb);
+    acc[TN][TM] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[TN], b[TM], acc[TN][TM], 0, 0, OPS, sa[TN], OPS,
+                                                                  sb[TM]);
+    if constexpr (TM + 1 < 4) mma_tiles<TN, TM + 1, OPS>(acc, a, b, sa, sb);
+    else if constexpr (TN + 1 < 4) mma_tiles<TN + 1, 0, OPS>(acc, a, b, sa, sb);
 }
 
-// All MFMAs of one LDS stage: two 64-byte k-steps of the wave's 4 x 4 tiles.
-__device__ __forceinline__ void mma_stage(v16f (&acc)[4][4], const uint8_t* stage, int wn, int wm, int c32, int hk)
+// Stage s = 2p + Q.  Lane (c32, hk) holds, of the 64 k of the stage, the bytes
+// k = 16*hk .. +15 and 32 + 16*hk .. +15 (chunks hk and 2 + hk) of its row, and
+// its scale byte covers the 32-k block hk: block 4p + 2Q + hk of the row, which
+// is byte 2Q of the pair's scale word shifted right by 8*hk.
+// MFMA I of the wave's 4 x 4 tiles, then (I < 8) data load I of stage t.
+template <int Q, int I>
+__device__ __forceinline__ void mma_step(v16f (&acc)[4][4], const v8i (&a)[4], const v8i (&b)[4], const int (&sa)[4],
+                                         const int (&sb)[4], const DataLoads& d, int t)
 {
-    const uint8_t* A = stage;
-    const uint8_t* B = stage + kTileBytes;
-    const uint8_t* SA = stage + 2 * kTileBytes;
-    const uint8_t* SB = SA + kScaleBytes;
+    constexpr int tn = I >> 2, tm = I & 3;
+    acc[tn][tm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[tn], b[tm], acc[tn][tm], 0, 0, 2 * Q, sa[tn],
+                                                                  2 * Q, sb[tm]);
+    if constexpr (I < 8) issue_data<I>(d, t);
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int Q, int... Is>
+__device__ __forceinline__ void mma_steps(v16f (&acc)[4][4], const v8i (&a)[4], const v8i (&b)[4], const int (&sa)[4],
+                                          const int (&sb)[4], const DataLoads& d, int t, std::integer_sequence<int, Is...>)
+{
+    (mma_step<Q, Is>(acc, a, b, sa, sb, d, t), ...);
+}
+
+// Stage s = 2p + Q: read its operands from LDS, then issue its 16 MFMAs with
+// the 8 data loads of stage t = s + 3 slotted one after each of the first 8
+// (the loads' issue stalls then overlap the matrix core).
+template <int Q>
+__device__ __forceinline__ void mma_stage(v16f (&acc)[4][4], const uint8_t* lds, int s, int wn, int wm, int c32,
+                                          int hk, const int (&sa)[4], const int (&sb)[4], const DataLoads& d, int t)
+{
+    const uint8_t* A = lds + (s & (kRing - 1)) * 2 * kTileBytes;
+    const uint8_t* B = A + kTileBytes;
+    v8i a[4], b[4];
 #pragma unroll
-    for (int j = 0; j < kBK / 64; ++j) {
-        const int kb = 2 * j + hk;
-        const int sa = *reinterpret_cast<const int*>(SA + kb * kBM + wn * 128 + c32 * 4);
-        const int sb = *reinterpret_cast<const int*>(SB + kb * kBM + wm * 128 + c32 * 4);
-        // operand bytes of lane (c32, hk) in the 64-byte k-step j: k = 16*hk .. +15
-        // and 32 + 16*hk .. +15, i.e. chunks 4j + hk and 4j + 2 + hk; its scale
-        // byte covers the 32-k block hk of the step (block 2j + hk of the stage)
-        v8i a[4], b[4];
+    for (int i = 0; i < 4; ++i) a[i] = read_frag(A, 128 * wn + 32 * i + c32, hk, 2 + hk);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) a[i] = read_frag(A, 128 * wn + 32 * i + c32, 4 * j + hk, 4 * j + 2 + hk);
+    for (int i = 0; i < 4; ++i) b[i] = read_frag(B, 128 * wm + 32 * i + c32, hk, 2 + hk);
+    __builtin_amdgcn_sched_barrier(0);
+    mma_steps<Q>(acc, a, b, sa, sb, d, t, std::make_integer_sequence<int, 16>{});
+}
+
+// Scale words of the pair of stage s (s even) for the lane's four A and B
+// tiles: word (s % 8) / 2 of each row's 16-byte chunk, shifted so that byte 2Q
+// is the lane's k-block.
+__device__ __forceinline__ void load_scales(int (&sa)[4], int (&sb)[4], const uint8_t* lds, int s, int wn, int wm,
+                                            int c32, int hk)
+{
+    const uint8_t* sl = lds + kDataBytes + ((s >> 3) & 1) * 2 * kChunkBytes + ((s & 7) >> 1) * 4;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) b[i] = read_frag(B, 128 * wm + 32 * i + c32, 4 * j + hk, 4 * j + 2 + hk);
-        mma_tiles<0, 0>(acc, a, b, sa, sb);
+    for (int i = 0; i < 4; ++i) {
+        sa[i] = (int)(*reinterpret_cast<const uint32_t*>(sl + (128 * wn + 32 * i + c32) * 16) >> (8 * hk));
+        sb[i] = (int)(*reinterpret_cast<const uint32_t*>(sl + kChunkBytes + (128 * wm + 32 * i + c32) * 16) >>
+                      (8 * hk));
     }
 }
 
@@ -304,7 +404,7 @@ void mm_tile_kernel(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ 
                     const uint8_t* __restrict__ wq, const uint8_t* __restrict__ wsc, int N, int K, int G,
                     const int* __restrict__ ws, void* __restrict__ y)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kStageBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
 
     const int V = ws[0];
     const int q = (V + kXcds - 1) / kXcds;
@@ -323,17 +423,17 @@ void mm_tile_kernel(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ 
     const int nrows_w = N - n0 < kBN ? N - n0 : kBN;
     const int nrows_x = tl.r1 - tl.r0;
     const size_t wrow0 = (size_t)tl.g * (size_t)N + (size_t)n0;
-    const Rsrc wr = make_rsrc(wq + wrow0 * uK, (uint32_t)nrows_w * uK);
-    const Rsrc xr = make_rsrc(xq + (size_t)tl.r0 * uK, (uint32_t)nrows_x * uK);
-    const Rsrc wsr = make_rsrc(wsc + wrow0 * KB, (uint32_t)nrows_w * KB);
-    const Rsrc xsr = make_rsrc(xs + (size_t)tl.r0 * KB, (uint32_t)nrows_x * KB);
+    const v4i wr = make_srd(wq + wrow0 * uK, (uint32_t)nrows_w * uK);
+    const v4i xr = make_srd(xq + (size_t)tl.r0 * uK, (uint32_t)nrows_x * uK);
+    const v4i wsr = make_srd(wsc + wrow0 * KB, (uint32_t)nrows_w * KB);
+    const v4i xsr = make_srd(xs + (size_t)tl.r0 * KB, (uint32_t)nrows_x * KB);
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int wn = wave >> 1;                    // W rows (output columns) 128*wn ..
     const int wm = wave & 1;                     // X rows (tokens) 128*wm ..
     const int c32 = lane & 31;
-    const int hk = lane >> 5;                    // which 32-byte half of a 64-byte k-step
+    const int hk = lane >> 5;
 
     v16f acc[4][4];
 #pragma unroll
@@ -343,25 +443,36 @@ void mm_tile_kernel(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ 
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-    const int nk = K / kBK;
-    StageRegs regs;
-    load_stage(regs, wr, xr, wsr, xsr, uK, 0);
-    store_stage(regs, lds);
-    __syncthreads();
-
-    // every stage but the last: prefetch the next stage while this one multiplies
-    for (int kt = 0; kt + 1 < nk; ++kt) {
-        // issue order: next stage's global loads, this stage's MFMAs, then the
-        // LDS writes (which wait for those loads) -- the loads land while the
-        // matrix core is busy.  The scheduling barriers keep that order.
-        load_stage(regs, wr, xr, wsr, xsr, uK, (kt + 1) * kBK);
-        __builtin_amdgcn_sched_barrier(0);
-        mma_stage(acc, lds + (kt & 1) * kStageBytes, wn, wm, c32, hk);
-        __builtin_amdgcn_sched_barrier(0);
-        store_stage(regs, lds + ((kt + 1) & 1) * kStageBytes);
-        __syncthreads();
+    // Pipeline: stages 0..2 in flight before the loop; the top of stage s
+    // waits for stage s (loads complete in issue order, and the scale chunk of
+    // s was issued with an earlier stage) and frees slot s-1 for stage s+3.
+    const int nk = K / kBK;                      // even, >= 2
+    DataLoads d;
+    d.wr = wr;
+    d.xr = xr;
+    d.nk = nk;
+    d.lds0 = lds_addr(lds + 64 * wave * kBK);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = 64 * wave + 16 * i + (lane >> 2);
+        d.off[i] = (uint32_t)row * uK + ((uint32_t)swz(row, lane & 3) << 4);
     }
-    mma_stage(acc, lds + ((nk - 1) & 1) * kStageBytes, wn, wm, c32, hk);
+    int sa[4], sb[4];
+    issue_stage(0, nk, wsr, xsr, KB, lds, wave, lane, d);
+    issue_stage(1, nk, wsr, xsr, KB, lds, wave, lane, d);
+    issue_stage(2, nk, wsr, xsr, KB, lds, wave, lane, d);
+    for (int s = 0; s < nk; s += 2) {
+        stage_wait();
+        issue_chunk(s + 3, nk, wsr, xsr, KB, lds, wave, lane);
+        load_scales(sa, sb, lds, s, wn, wm, c32, hk);
+        mma_stage<0>(acc, lds, s, wn, wm, c32, hk, sa, sb, d, s + 3);
+        stage_wait();
+        issue_chunk(s + 4, nk, wsr, xsr, KB, lds, wave, lane);
+        mma_stage<1>(acc, lds, s + 1, wn, wm, c32, hk, sa, sb, d, s + 4);
+    }
+    // the last three stages' loads read zeros into unused slots; let them land
+    // before the workgroup's LDS goes away
+    stage_barrier<0>();
 
     // epilogue: lane holds D[n][m] for m = c32 and n = 8*(e/4) + 4*hk + e%4
 #pragma unroll
@@ -396,7 +507,7 @@ int grouped_mm_max_groups() { return kMaxGroups; }
 bool grouped_mm_sizes_ok(int64_t M, int64_t N, int64_t K, int64_t G)
 {
     if (M < 0 || N < 0 || K < 0 || G < 1 || G > kMaxGroups) return false;
-    if (K % kBK != 0 || N % 8 != 0) return false;
+    if (K % kKStep != 0 || N % 8 != 0) return false;
     // K <= 2^23 keeps a tile's 256 rows of K bytes within a 32-bit buffer resource
     if (M >= ((int64_t)1 << 31) || N >= ((int64_t)1 << 31) || K > ((int64_t)1 << 23)) return false;
     const int64_t nc = (N + kBN - 1) / kBN;
