@@ -20,6 +20,15 @@ each output written once) over time.  Inputs are resident in device memory
 before timing starts; several independent buffer sets are rotated so that no
 step finds the previous step's data in the 256 MB last-level cache.
 
+The JSON line also carries, under "grouped_mm", the next row of the path timed
+on its own (it is not part of the step or of `value`): the MXFP8 scaled grouped
+GEMM of the MoE configuration -- tokens (16640, 5120) routed to 16 experts
+(Zipf 1.1), expert weights (16, 8192, 5120) ~ N(0, 0.02^2), both quantized with
+mxq_quantize_mx, Y_g = X_g W_g^T on the scaled-fp8 MFMA, bf16 out -- with its
+own roofline against the dense fp8 matrix peak (5.0 PFLOP/s).  Sources:
+"[float8] add float8 rowwise MoE prototype" (Summary) and "[mxfp8 MoE training]
+Support mxfp8 all to all in expert parallel" (Performance: MXFP8 grouped GEMMs).
+
 Prints ONE JSON line (see the keys below).  --gpus N > 1 is refused: this path
 runs on one GPU.
 """
@@ -38,6 +47,8 @@ HBM_PEAK_GBPS = 8000.0                     # MI355X HBM3E, 8 TB/s
 DISPATCH = (65536, 5120)
 TOKENS = (16640, 5120)
 G_ROW, G_COL = 16, 128
+EXPERTS = (16, 8192, 5120)                 # (G, N, K) of the grouped GEMM
+MFMA_FP8_PEAK_TFLOPS = 5000.0              # MI355X dense fp8 matrix peak
 PROFILES = os.path.join(HERE, "profiles")
 TRAFFIC_FILE = os.path.join(PROFILES, "traffic_counters.json")
 
@@ -69,6 +80,7 @@ def parse_args():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--rotate", type=int, default=4, help="independent buffer sets cycled through")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-gemm", action="store_true", help="skip the grouped GEMM leg")
     p.add_argument("--cpu-mx-rows", type=int, default=16384, help="dispatch rows in the CPU sample")
     p.add_argument("--cpu-group-rows", type=int, default=8320, help="token rows in the CPU sample")
     p.add_argument("--ingest-counters", nargs="+", metavar="CSV",
@@ -183,6 +195,71 @@ def cpu_info():
     except AttributeError:
         n = os.cpu_count()
     return model, n
+
+
+def bench_grouped_mm(args, dev, stream, x_host, ends, W, mxq, np, torch):
+    """Quantize tokens and expert weights with libmxq, then time the scaled grouped
+    GEMM alone (two token buffer sets alternate; the 671 MB of fp8 weights exceed
+    the last-level cache by themselves)."""
+    G, N, K = EXPERTS
+    M = x_host.shape[0]
+    offs = torch.from_numpy(ends).to(dev)
+    w_host = W.expert_weights(G, N, K, seed=2)
+    w_dev = w_host.to(dev).view(G * N, K)
+    del w_host
+    wq = torch.empty((G * N, K), dtype=torch.uint8, device=dev)
+    wsc = torch.empty((G * N, K // 32), dtype=torch.uint8, device=dev)
+    x_dev = x_host.to(dev)
+    xsets = []
+    for _ in range(2):
+        xq = torch.empty((M, K), dtype=torch.uint8, device=dev)
+        xs = torch.empty((M, K // 32), dtype=torch.uint8, device=dev)
+        mxq.mxq_quantize_mx(x_dev, xq, xs, stream)
+        xsets.append((xq, xs))
+    # time the weight quantization too (context: it runs once per weight update)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    mxq.mxq_quantize_mx(w_dev, wq, wsc, stream)
+    e0.record(stream)
+    mxq.mxq_quantize_mx(w_dev, wq, wsc, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wquant_us = e0.elapsed_time(e1) * 1e3
+    del w_dev, x_dev
+    wq3 = wq.view(G, N, K)
+    ws3 = wsc.view(G, N, K // 32)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    wsp = torch.empty(max(mxq.mxq_grouped_mm_workspace_bytes(M, N, K, G), 16), dtype=torch.uint8, device=dev)
+
+    def call(i):
+        xq, xs = xsets[i % 2]
+        mxq.mxq_scaled_grouped_mm(xq, xs, wq3, ws3, offs, y, wsp, stream)
+
+    for i in range(3):
+        call(i)
+    torch.cuda.synchronize()
+    reps = max(10, args.steps // 2)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for i in range(reps):
+        evs[i][0].record(stream)
+        call(i)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    times = sorted(e[0].elapsed_time(e[1]) * 1e3 for e in evs)
+    med = times[len(times) // 2]
+    rows = int(ends[-1])                                  # routed rows (all of them here)
+    flops = 2.0 * rows * N * K
+    tflops = flops / (med * 1e6)
+    return {
+        "workload": (f"MXFP8 scaled grouped GEMM: tokens ({M}, {K}) in {G} Zipf(1.1) groups x expert "
+                     f"weights ({G}, {N}, {K}), bf16 out; operands quantized with mxq_quantize_mx"),
+        "avg_us": round(float(np.mean(times)), 1), "median_us": round(med, 1), "min_us": round(times[0], 1),
+        "TFLOPs": round(tflops, 1),
+        "roofline": {"bound": "mfma", "kernel": "mm_tile_kernel", "achieved": round(tflops, 1),
+                     "peak": MFMA_FP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / MFMA_FP8_PEAK_TFLOPS, 4),
+                     "flops_per_launch": flops, "timed": "median of per-launch events (plan + tile kernels)"},
+        "weight_quantize_us": round(wquant_us, 1),
+        "operand_bytes": M * K * (1 + 1 / 32) + G * N * K * (1 + 1 / 32) + 2 * M * N,
+    }
 
 
 def main():
@@ -355,6 +432,9 @@ def main():
                 "traffic_note": traffic_note, "algorithmic_bytes_per_launch": call_bytes[dom],
                 "avg_launch_us": round(dom_us, 2)}
 
+    # ------------------------------------------------------ grouped GEMM --
+    grouped_mm = None if args.no_gemm else bench_grouped_mm(args, dev, stream, x2_host, ends16, W, mxq, np, torch)
+
     # --------------------------------------------------------- CPU baseline --
     cpu_baseline = None
     if not args.no_cpu_baseline:
@@ -415,6 +495,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu_baseline,
         "kernels": kernels,
+        "grouped_mm": grouped_mm,
         "kernels_method": "each call alone, back to back over the rotated buffer sets, events at both ends",
         "copy_ceiling_GBps": round(copy_gbps, 1),
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""), "cus": props.multi_processor_count},

@@ -26,18 +26,17 @@
 //   stretch of the list and its L2 sees the reuse.
 //
 // Tile kernel (256 threads = 4 waves in 2 x 2, each wave 128 x 128)
-//   K advances 128 bytes per stage through a double-buffered LDS (2 x 66 KB):
-//   the W_g and X tiles (256 rows x 128 B each; 16-byte chunks XOR-swizzled by
-//   row so that fragment reads and tile writes are free of bank conflicts) and
-//   their E8M0 scales (transposed so that one 32-bit LDS read gives a lane the
-//   scale bytes of its four 32-row MFMA tiles; the instruction's op_sel picks
-//   the byte).  Global loads are raw buffer loads whose resource ends at the
-//   tile's last valid row: rows past a group's end or past N read as zero, with
-//   no per-row branch.  One barrier per stage: the loads of stage s+1 are in
-//   flight while the MFMAs of stage s run.  MFMA operand A is W_g (output
-//   columns), B is X (token rows), so each lane ends up holding runs of four
-//   consecutive output columns of one row and stores them as one 8-byte
-//   (bf16) or 16-byte (fp32) write.
+//   K advances 64 bytes (one MFMA k-step) per stage through a 4-slot LDS ring
+//   of W_g and X tiles (256 rows x 64 B each; 16-byte chunks XOR-swizzled by
+//   row so that the operand reads are free of bank conflicts), filled straight
+//   from global memory by buffer-load-to-LDS.  Each stage waits for its own
+//   loads, reads the wave's operands into VGPRs, and issues its 16 MFMAs with
+//   the loads of the stage three ahead slotted between them.  Global loads use
+//   raw buffer resources that end at the tile's last valid row: rows past a
+//   group's end or past N read as zero, with no per-row branch.  MFMA operand
+//   A is W_g (output columns), B is X (token rows), so each lane ends up holding
+//   runs of four consecutive output columns of one row and stores them as one
+//   8-byte (bf16) or 16-byte (fp32) write.
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -185,10 +184,8 @@ __global__ __launch_bounds__(kPlanThreads) void mm_plan_kernel(const int32_t* __
 // K advances kBK = 64 bytes (one MFMA k-step) per stage.  Stages live in a
 // 4-deep LDS ring filled by buffer-load-to-LDS (the data never passes through
 // VGPRs), so three stages are in flight while one is multiplied.  Scales
-// travel in chunks of 16 bytes per row (16 k-blocks = 8 stages), fetched four
-// stages before their first use into a 2-slot ring: one 16-byte request per
-// row instead of one 4-byte request per row per stage pair, which matters
-// because the L1's outstanding-request budget, not bytes, bounds the feed.
+// travel in chunks of 16 bytes per row (16 k-blocks = 8 stages), fetched seven
+// stages before their first use into a 2-slot ring.
 constexpr int kRing = 4;
 constexpr int kChunkStages = 8;                         // stages per scale chunk
 constexpr int kTileBytes = kBM * kBK;                   // 16 KB of codes per operand per stage
