@@ -64,27 +64,26 @@
 namespace mxq {
 
 constexpr int kGThreads = 256;      // plan kernel
-constexpr int kTThreads = 512;      // hold and deferred kernels
-constexpr int kHold = 16;           // rows of 8 columns held per lane
-
 template <int LAYOUT>
 struct TileCfg;
 template <>
 struct TileCfg<0> {                 // row-major output
-    static constexpr int R = 128, W = 512;
+    static constexpr int T = 512, H = 16, W = 512;
     static constexpr int CG = W / 8;                  // 8-column groups per strip (lanes per row)
-    static constexpr int NS = kTThreads / CG;         // lanes sharing the same columns
+    static constexpr int NS = T / CG;                 // lanes sharing the same columns
+    static constexpr int R = NS * H;
     __device__ static int row(int rs, int i) { return rs + NS * i; }
 };
 template <>
 struct TileCfg<1> {                 // column-major output
-    static constexpr int R = 128, W = 512;
+    static constexpr int T = 512, H = 16, W = 512;
     static constexpr int CG = W / 8;
-    static constexpr int NS = kTThreads / CG;
-    __device__ static int row(int rs, int i) { return rs * kHold + i; }
+    static constexpr int NS = T / CG;
+    static constexpr int R = NS * H;
+    __device__ static int row(int rs, int i) { return rs * H + i; }
 };
-static_assert(TileCfg<0>::NS * kHold == TileCfg<0>::R, "row tile shape");
-static_assert(TileCfg<1>::NS * kHold == TileCfg<1>::R, "col tile shape");
+static_assert(TileCfg<1>::R == 128, "col tile shape");
+static_assert(TileCfg<0>::R == 128, "row tile shape");
 
 // Values that no finished result takes: a scale is a positive float or the
 // canonical NaN 0x7FC00000, a column maximum of |bf16| bits is at most 0x7FFF.
@@ -217,6 +216,19 @@ __device__ __forceinline__ uint4 abs8(uint4 v)
     return make_uint4(v.x & 0x7FFF7FFFu, v.y & 0x7FFF7FFFu, v.z & 0x7FFF7FFFu, v.w & 0x7FFF7FFFu);
 }
 
+// a = max(a, red[1..n-1][cg]), two LDS rows per step so that few registers are
+// live while a tile is held.
+__device__ __forceinline__ void max_rows(uint4& a, const uint4* red, int n, int stride)
+{
+#pragma unroll 1
+    for (int r = 1; r < n; r += 2) {
+        const uint4 b0 = red[r * stride];
+        const uint4 b1 = r + 1 < n ? red[(r + 1) * stride] : make_uint4(0, 0, 0, 0);
+        max8(a, b0);
+        max8(a, b1);
+    }
+}
+
 // Everything a tile needs to know about itself.
 struct TileInfo {
     int g, r0, r1;        // group (G = rows past the last end) and its rows [r0, r1)
@@ -265,10 +277,14 @@ __device__ __forceinline__ uint4 load_coherent(const void* p)
 }
 
 // ------------------------------------------------------ buffer accesses ---
-// Raw buffer loads through a (base, size) resource: an offset at or past the
-// size reads zero without touching memory.
+// Raw buffer accesses through a (base, size) resource: at an offset at or past
+// the size a load reads zero and a store is dropped, without touching memory.
+// X is read once and the codes written once, so both use the streaming
+// (non-temporal) cache policy, which measured about 10 % faster in the hold
+// kernel than the default one.
 typedef __amdgpu_buffer_rsrc_t Rsrc;
 constexpr uint32_t kOOB = 0xFFFFFFF0u;      // above every resource size used here (at most 2^31)
+constexpr int kNonTemporal = 2;             // cache-policy operand of the buffer builtins: nt
 
 __device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes)
 {
@@ -277,28 +293,63 @@ __device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes)
 
 __device__ __forceinline__ uint4 buf_load16(Rsrc r, uint32_t off)
 {
-    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNonTemporal);
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-// Load this lane's 16 rows x 8 columns of the tile (zeros outside rows/columns).
+__device__ __forceinline__ void buf_store8(uint2 v, Rsrc r, uint32_t off)
+{
+    const u32x2 w = {v.x, v.y};
+    __builtin_amdgcn_raw_buffer_store_b64(w, r, off, 0, kNonTemporal);
+}
+
+// An opaque copy: the compiler cannot relate the result to its input, so
+// offsets derived from it are recomputed where used instead of being kept in
+// registers from an earlier phase.
+__device__ __forceinline__ int opaque(int v)
+{
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
+// First index i of this lane's rows (C::row(rs, i), increasing in i) at or past
+// tile row `lo`; C::H when the lane's columns are past K.
 template <int LAYOUT>
-__device__ __forceinline__ void load_tile(const uint16_t* __restrict__ x, int K, const TileInfo& t, int k, int rs,
-                                          uint4 v[kHold])
+__device__ __forceinline__ int first_held_row(int lo, int rs, bool col_ok)
 {
     using C = TileCfg<LAYOUT>;
-    // Raw buffer loads over rows [a, r1) of the tile (at most 128 rows x 2^24
-    // bytes): rows past r1 fall outside the resource and rows before r0 or
-    // columns past K get an offset outside it, and such loads read zero with no
-    // memory traffic.  Masking by offset instead of by branch lets all kHold
-    // loads be in flight at once.
-    const Rsrc r = make_rsrc(x + (int64_t)t.a * K, (uint32_t)(t.r1 - t.a) * (uint32_t)K * 2u);
-    const int lo = t.r0 - t.a;
+    int i0 = 0;
+    if (LAYOUT == 0)
+        i0 = lo > rs ? (lo - rs + C::NS - 1) / C::NS : 0;
+    else
+        i0 = lo > rs * C::H ? lo - rs * C::H : 0;
+    return col_ok ? i0 : C::H;
+}
+
+// Load this lane's H rows x 8 columns of the tile (zeros outside rows/columns).
+template <int LAYOUT>
+__device__ __forceinline__ void load_tile(const uint16_t* __restrict__ x, int K, const TileInfo& t, int k, int rs,
+                                          uint4 (&v)[TileCfg<LAYOUT>::H])
+{
+    using C = TileCfg<LAYOUT>;
+    // Raw buffer loads, one resource per 128 rows of the tile (at most 2^31
+    // bytes each) clipped to rows [a, r1): rows past r1 fall outside the
+    // resource and rows before r0 or columns past K get an offset outside it,
+    // and such loads read zero with no memory traffic.  Masking by offset
+    // instead of by branch lets all H loads be in flight at once.
+    constexpr int NR = C::R > 128 ? C::R / 128 : 1;      // 128-row resources
+    constexpr int PER = C::H / NR;                        // lane rows per resource
+    const int i0 = first_held_row<LAYOUT>(t.r0 - t.a, rs, k < K);
+    const uint32_t base = ((uint32_t)(C::row(rs, 0)) * (uint32_t)K + (uint32_t)k) * 2u;
+    const uint32_t step = (uint32_t)(C::row(0, 1) - C::row(0, 0)) * (uint32_t)K * 2u;
 #pragma unroll
-    for (int i = 0; i < kHold; ++i) {
-        const int rt = C::row(rs, i);
-        const uint32_t off = (k < K && rt >= lo) ? ((uint32_t)rt * (uint32_t)K + (uint32_t)k) * 2u : kOOB;
-        v[i] = buf_load16(r, off);
+    for (int h = 0; h < NR; ++h) {
+        const int hi = t.r1 - t.a - 128 * h;
+        const uint32_t rows = hi <= 0 ? 0u : hi >= 128 ? 128u : (uint32_t)hi;
+        const Rsrc r = make_rsrc(x + (int64_t)(t.a + 128 * h) * K, rows * (uint32_t)K * 2u);
+#pragma unroll
+        for (int i = h * PER; i < (h + 1) * PER; ++i)
+            v[i] = buf_load16(r, i >= i0 ? base + (uint32_t)(i - h * PER) * step : kOOB);
     }
 }
 
@@ -338,20 +389,21 @@ __device__ __forceinline__ void store_partial16(uint4 val, uint8_t* dst, int lo,
 // Quantize the held rows and store them in the output layout.  `stage` is the
 // LDS staging tile (column layout only).
 template <int LAYOUT>
-__device__ __forceinline__ void quantize_store_tile(const uint4 v[kHold], const ColScales& cs, const TileInfo& t,
+__device__ __forceinline__ void quantize_store_tile(const uint4 (&v)[TileCfg<LAYOUT>::H], const ColScales& cs, const TileInfo& t,
                                                     int M, int K, int k, int cg, int rs, uint8_t* __restrict__ q,
                                                     uint8_t* stage, bool zero)
 {
     using C = TileCfg<LAYOUT>;
     if (LAYOUT == 0) {
-        if (k >= K) return;
+        // buffer stores over rows [a, r1) (at most 256 x 2^23 bytes): a row before
+        // r0 or a column past K gets an offset outside the resource and is dropped
+        const Rsrc r = make_rsrc(q + (int64_t)t.a * K, (uint32_t)(t.r1 - t.a) * (uint32_t)K);
+        const int i0 = first_held_row<LAYOUT>(t.r0 - t.a, opaque(rs), k < K);
+        const uint32_t base = (uint32_t)opaque(rs) * (uint32_t)K + (uint32_t)k;
 #pragma unroll
-        for (int i = 0; i < kHold; ++i) {
-            const int row = t.a + C::row(rs, i);
-            if (row >= t.r0 && row < t.r1) {
-                const uint2 out = zero ? make_uint2(0, 0) : group_quantize_chunk(v[i], cs);
-                *(uint2*)(q + (int64_t)row * K + k) = out;
-            }
+        for (int i = 0; i < C::H; ++i) {
+            const uint32_t off = i >= i0 ? base + (uint32_t)(i * C::NS) * (uint32_t)K : kOOB;
+            buf_store8(zero ? make_uint2(0, 0) : group_quantize_chunk(v[i], cs), r, off);
         }
     } else {
         // Pair the same column of consecutive rows in each conversion, so that
@@ -376,15 +428,15 @@ __device__ __forceinline__ void quantize_store_tile(const uint4 v[kHold], const 
                 pk = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], pk, true);
                 d[b] = (zero ? 0u : col_nan ? 0x7F7F7F7Fu : (uint32_t)pk);
             }
-            *(uint4*)(stage + col_tile_offset(cg * 8 + c, rs * kHold)) = make_uint4(d[0], d[1], d[2], d[3]);
+            *(uint4*)(stage + col_tile_offset(cg * 8 + c, rs * C::H)) = make_uint4(d[0], d[1], d[2], d[3]);
         }
         __syncthreads();
         // column cc of the tile becomes output row (strip * W + cc): rows [lo, hi) of the tile
         const int lo = t.r0 - t.a, hi = t.r1 - t.a;
         const bool aligned16 = (M & 15) == 0;
         const int64_t col0 = (int64_t)t.s * C::W;
-        for (int it = 0; it < (C::W * 8) / kTThreads; ++it) {
-            const int sid = (int)threadIdx.x + kTThreads * it;
+        for (int it = 0; it < (C::W * 8) / C::T; ++it) {
+            const int sid = (int)threadIdx.x + C::T * it;
             const int cc = sid >> 3, seg = sid & 7;
             if (col0 + cc >= K) continue;
             const int rb = seg * 16;
@@ -394,7 +446,7 @@ __device__ __forceinline__ void quantize_store_tile(const uint4 v[kHold], const 
             const uint4 val = *(const uint4*)(stage + col_tile_offset(cc, rb));
             uint8_t* dst = q + (col0 + cc) * (int64_t)M + t.a + rb;
             if (aligned16 && a == rb && e == rb + 16) {
-                *(uint4*)dst = val;
+                store_nt(val, (uint4*)dst);
             } else {
                 store_partial16(val, dst, a - rb, e - rb, aligned16);
             }
@@ -580,72 +632,99 @@ __device__ __forceinline__ void write_empty_group_scales(int G, int K, const Wor
     }
 }
 
-// Column maxima of the held tile, published as one row of the partials by the
-// lanes with rs == 0 (all in wave 0), then the tile counts itself in.  No
-// ordering between the two is needed: the partial row carries its own "not yet
-// written" value and the last arrival polls it.  Returns 1 in every lane of
-// the last tile of its (group, strip) to arrive.
+// Column maxima of the held tile: reduced over the tile's rows through LDS and
+// published as the tile's row of the partial maxima by the lanes with rs == 0,
+// which return the maxima of their 8 columns (other lanes return zeros).
 template <int LAYOUT, class Sh>
-__device__ __forceinline__ int publish_and_count(const uint4 v[kHold], const TileInfo& t, int j, int s, int K, int S,
-                                                 int k, int cg, int rs, const Workspace& ws, bool streamed, Sh& sh)
+__device__ __forceinline__ uint4 publish_tile_max(const uint4 (&v)[TileCfg<LAYOUT>::H], int j, int K, int k, int cg,
+                                                  int rs, const Workspace& ws, Sh& sh)
 {
     using C = TileCfg<LAYOUT>;
     uint4 m = abs8(v[0]);
 #pragma unroll
-    for (int i = 1; i < kHold; ++i) max8(m, abs8(v[i]));
+    for (int i = 1; i < C::H; ++i) max8(m, abs8(v[i]));
     sh.red[rs][cg] = m;
     __syncthreads();
     if (rs == 0) {
-#pragma unroll
-        for (int r = 1; r < C::NS; ++r) max8(m, sh.red[r][cg]);
+        max_rows(m, &sh.red[0][cg], C::NS, C::CG);
         if (k < K) store_coherent(m, ws.partial + (int64_t)j * K + k);
+    } else {
+        m = make_uint4(0, 0, 0, 0);
     }
+    __syncthreads();                                      // sh.red is reused by the strip reduction
+    return m;
+}
+
+// Streamed groups: publish the tile's maxima, then count the tile in.  Returns 1
+// in every lane of the last tile of its (group, strip) to arrive.  No ordering
+// between the partial row and the count is needed: the partial row carries its
+// own "not yet written" value and the last arrival polls it.
+template <int LAYOUT, class Sh>
+__device__ __forceinline__ int publish_and_count(const uint4 (&v)[TileCfg<LAYOUT>::H], const TileInfo& t, int j, int s,
+                                                 int K, int S, int k, int cg, int rs, const Workspace& ws, Sh& sh)
+{
+    publish_tile_max<LAYOUT>(v, j, K, k, cg, rs, ws, sh);
     if (threadIdx.x == 0) {
         const uint32_t old = __hip_atomic_fetch_add(ws.count + (int64_t)t.g * S + s, 1u, __ATOMIC_RELAXED,
                                                     __HIP_MEMORY_SCOPE_AGENT);
-        if (streamed) __hip_atomic_store(ws.any, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(ws.any, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         sh.state = (old + 1 == (uint32_t)t.count) ? 1 : 0;
     }
     __syncthreads();
     return sh.state;
 }
 
-// Last arrival: reduce the strip's partial rows over the group's chunks (each
-// polled until written; if one never comes, from the input instead), divide,
+// Reduce the strip's partial rows over the group's chunks, except chunk `skip`
+// whose maxima the rs == 0 lanes bring in `own` (zeros otherwise), divide,
 // store the scales (`scales_coherent`: with agent-scope stores, for readers in
-// the same launch) and leave this lane's 8 scales in `cs`.
+// the same launch) and leave this lane's 8 scales in `cs`.  Each lane polls its
+// rows in batches: every round trip re-reads all rows of the batch not yet
+// written, so the batch completes one round trip after its last row lands.  If
+// a row does not come within the time limit, the maxima are taken from the
+// input instead.
+constexpr int kPollBatch = 4;
 template <int LAYOUT, class Sh>
 __device__ __forceinline__ void reduce_strip(const uint16_t* __restrict__ x, const TileInfo& t, int K, int k, int cg,
-                                             int rs, const Workspace& ws, float* __restrict__ scales,
-                                             bool scales_coherent, unsigned long long timeout_ticks, Sh& sh,
-                                             ColScales& cs)
+                                             int rs, const Workspace& ws, float* __restrict__ scales, int skip,
+                                             uint4 own, bool scales_coherent, unsigned long long timeout_ticks,
+                                             Sh& sh, ColScales& cs)
 {
     using C = TileCfg<LAYOUT>;
-    uint4 a = make_uint4(0, 0, 0, 0);
+    uint4 a = own;
     int ok = 1;
     if (k < K) {
         const uint16_t* p = ws.partial + (int64_t)t.first * K + k;
-        for (int c0 = rs; c0 < t.count; c0 += 4 * C::NS) {
-            uint4 b[4];
+        const int skip_c = skip - t.first;
+        for (int c0 = rs; c0 < t.count && ok; c0 += kPollBatch * C::NS) {
+            uint32_t pending = 0;
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
-                b[u] = c0 + u * C::NS < t.count ? load_coherent(p + (int64_t)(c0 + u * C::NS) * K) : make_uint4(0, 0, 0, 0);
+            for (int u = 0; u < kPollBatch; ++u) {
+                const int c = c0 + u * C::NS;
+                if (c < t.count && c != skip_c) pending |= 1u << u;
+            }
+            unsigned long long t0 = 0;
+            bool timing = false;
+            while (pending != 0u) {
+                uint4 b[kPollBatch];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                if (!partial_written(b[u])) {
-                    const unsigned long long t0 = wall_clock64();
-                    while (true) {
-                        __builtin_amdgcn_s_sleep(1);
-                        b[u] = load_coherent(p + (int64_t)(c0 + u * C::NS) * K);
-                        if (partial_written(b[u])) break;
-                        if (wall_clock64() - t0 > timeout_ticks) {
-                            ok = 0;
-                            b[u] = make_uint4(0, 0, 0, 0);
-                            break;
-                        }
+                for (int u = 0; u < kPollBatch; ++u)
+                    b[u] = (pending >> u) & 1u ? load_coherent(p + (int64_t)(c0 + u * C::NS) * K) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+                for (int u = 0; u < kPollBatch; ++u) {
+                    if (((pending >> u) & 1u) && partial_written(b[u])) {
+                        max8(a, b[u]);
+                        pending &= ~(1u << u);
                     }
                 }
-                max8(a, b[u]);
+                if (pending == 0u) break;
+                if (!timing) {
+                    t0 = wall_clock64();
+                    timing = true;
+                } else if (wall_clock64() - t0 > timeout_ticks) {
+                    ok = 0;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
             }
         }
     }
@@ -653,8 +732,7 @@ __device__ __forceinline__ void reduce_strip(const uint16_t* __restrict__ x, con
     sh.red[rs][cg] = a;
     __syncthreads();
     if (rs == 0) {
-#pragma unroll
-        for (int r = 1; r < C::NS; ++r) max8(a, sh.red[r][cg]);
+        max_rows(a, &sh.red[0][cg], C::NS, C::CG);
         const float4 lo = scales_lo(a), hi = scales_hi(a);
         *(float4*)(sh.scale + cg * 8) = lo;
         *(float4*)(sh.scale + cg * 8 + 4) = hi;
@@ -675,7 +753,7 @@ __device__ __forceinline__ void reduce_strip(const uint16_t* __restrict__ x, con
 
 // ---------------------------------------------------------------- hold ----
 template <int LAYOUT>
-__global__ __launch_bounds__(kTThreads)
+__global__ __launch_bounds__(TileCfg<LAYOUT>::T)
 void group_hold_kernel(const uint16_t* __restrict__ x, int M, int K, int G, int S, int SB, int slots, Workspace ws,
                        float* __restrict__ scales, uint8_t* __restrict__ q, int hold_limit,
                        unsigned long long timeout_ticks, int deferred_launched)
@@ -684,13 +762,13 @@ void group_hold_kernel(const uint16_t* __restrict__ x, int M, int K, int G, int 
     __shared__ TileShared<LAYOUT> sh;
     int j, s;
     tile_of_block((int)blockIdx.x, slots, SB, j, s);
-    write_empty_group_scales(G, K, ws, scales, kTThreads);
+    write_empty_group_scales(G, K, ws, scales, C::T);
     const TileInfo t = tile_info<C::R>(ws.table, j, s);
     if (t.g < 0) return;                                  // unused chunk id (uniform)
     const int cg = (int)threadIdx.x % C::CG, rs = (int)threadIdx.x / C::CG;
     const int k = s * C::W + cg * 8;
     ColScales cs;
-    uint4 v[kHold];
+    uint4 v[C::H];
 
     if (t.g == G) {                                       // rows past the last end: zeros
         quantize_store_tile<LAYOUT>(v, cs, t, M, K, k, cg, rs, q, sh.stage, true);
@@ -701,11 +779,20 @@ void group_hold_kernel(const uint16_t* __restrict__ x, int M, int K, int G, int 
     const bool streamed = t.count > hold_limit;
     load_tile<LAYOUT>(x, K, t, k, rs, v);
 
-    if (publish_and_count<LAYOUT>(v, t, j, s, K, S, k, cg, rs, ws, streamed, sh)) {
-        reduce_strip<LAYOUT>(x, t, K, k, cg, rs, ws, scales, true, timeout_ticks, sh, cs);
-        if (streamed) return;                             // the deferred kernel writes this group
+    if (streamed) {
+        // too many tiles to hold: the last arrival reduces the strip and the
+        // deferred kernel quantizes the group
+        if (publish_and_count<LAYOUT>(v, t, j, s, K, S, k, cg, rs, ws, sh))
+            reduce_strip<LAYOUT>(x, t, K, k, cg, rs, ws, scales, -1, make_uint4(0, 0, 0, 0), false, timeout_ticks,
+                                 sh, cs);
+        return;
+    }
+    // The group's last chunk, launched after all the others, reduces the strip
+    // (its own maxima straight from registers); the others publish and wait.
+    const uint4 own = publish_tile_max<LAYOUT>(v, j, K, k, cg, rs, ws, sh);
+    if (j == t.first + t.count - 1) {
+        reduce_strip<LAYOUT>(x, t, K, k, cg, rs, ws, scales, j, own, true, timeout_ticks, sh, cs);
     } else {
-        if (streamed) return;
         // wait for the strip's scales: the rs == 0 lanes poll their 8 columns
         // (bounded in wall-clock time) and pass them on through LDS
         int ok = 1;
@@ -744,8 +831,7 @@ void group_hold_kernel(const uint16_t* __restrict__ x, int M, int K, int G, int 
             sh.red[rs][cg] = a;
             __syncthreads();
             if (rs == 0) {
-#pragma unroll
-                for (int r = 1; r < C::NS; ++r) max8(a, sh.red[r][cg]);
+                max_rows(a, &sh.red[0][cg], C::NS, C::CG);
                 *(float4*)(sh.scale + cg * 8) = scales_lo(a);
                 *(float4*)(sh.scale + cg * 8 + 4) = scales_hi(a);
             }
@@ -765,7 +851,7 @@ void group_hold_kernel(const uint16_t* __restrict__ x, int M, int K, int G, int 
 // Amax pass: one workgroup per tile (the hold kernel's tiles); its column
 // maxima become the tile's piece of the chunk's partial row.
 template <int LAYOUT>
-__global__ __launch_bounds__(kTThreads)
+__global__ __launch_bounds__(TileCfg<LAYOUT>::T)
 void group_amax_kernel(const uint16_t* __restrict__ x, int K, int G, int S, Workspace ws)
 {
     using C = TileCfg<LAYOUT>;
@@ -775,11 +861,11 @@ void group_amax_kernel(const uint16_t* __restrict__ x, int K, int G, int S, Work
     if (t.g < 0 || t.g == G) return;                      // unused chunk id or rows past the last end (uniform)
     const int cg = (int)threadIdx.x % C::CG, rs = (int)threadIdx.x / C::CG;
     const int k = s * C::W + cg * 8;
-    uint4 v[kHold];
+    uint4 v[C::H];
     load_tile<LAYOUT>(x, K, t, k, rs, v);
     uint4 m = abs8(v[0]);
 #pragma unroll
-    for (int i = 1; i < kHold; ++i) max8(m, abs8(v[i]));
+    for (int i = 1; i < C::H; ++i) max8(m, abs8(v[i]));
     red[rs][cg] = m;
     __syncthreads();
     if (rs == 0 && k < K) {
@@ -825,7 +911,7 @@ void group_finalize_kernel(int K, int SF, Workspace ws, float* __restrict__ scal
 }
 
 template <int LAYOUT>
-__global__ __launch_bounds__(kTThreads)
+__global__ __launch_bounds__(TileCfg<LAYOUT>::T)
 void group_quant_kernel(const uint16_t* __restrict__ x, int M, int K, int G, int S, Workspace ws,
                         const float* __restrict__ scales, uint8_t* __restrict__ q)
 {
@@ -837,7 +923,7 @@ void group_quant_kernel(const uint16_t* __restrict__ x, int M, int K, int G, int
     const int cg = (int)threadIdx.x % C::CG, rs = (int)threadIdx.x / C::CG;
     const int k = s * C::W + cg * 8;
     ColScales cs;
-    uint4 v[kHold];
+    uint4 v[C::H];
     if (t.g < G) {
         load_tile<LAYOUT>(x, K, t, k, rs, v);
         if (k < K)
@@ -867,7 +953,7 @@ __device__ __forceinline__ void transpose4x4_bytes(uint32_t w0, uint32_t w1, uin
     out[3] = __builtin_amdgcn_perm(t23_hi, t01_hi, 0x07060302u);
 }
 
-__global__ __launch_bounds__(kTThreads)
+__global__ __launch_bounds__(TileCfg<1>::T)
 void group_quant_col_blocks_kernel(const uint16_t* __restrict__ x, int M, int K, int G, int S, Workspace ws,
                                    const float* __restrict__ scales, uint8_t* __restrict__ q)
 {
@@ -882,18 +968,18 @@ void group_quant_col_blocks_kernel(const uint16_t* __restrict__ x, int M, int K,
     t.r0 = a;
     t.r1 = a + C::R < M ? a + C::R : M;
     t.s = s;
-    uint4 v[kHold];
+    uint4 v[C::H];
     load_tile<1>(x, K, t, k, rs, v);
 
     // codes of this lane's 16 rows, row by row, each with its group's scales
-    const int row0 = a + rs * kHold;
+    const int row0 = a + rs * C::H;
     int g = ws.bfirst[blk];
     int gend = g < G ? ws.gend[g] : 0x7FFFFFFF;
     ColScales cs;
     bool have = false;
-    uint2 out[kHold];
+    uint2 out[C::H];
 #pragma unroll
-    for (int i = 0; i < kHold; ++i) {
+    for (int i = 0; i < C::H; ++i) {
         const int row = row0 + i;
         if (row >= gend) {
             do {
@@ -925,7 +1011,7 @@ void group_quant_col_blocks_kernel(const uint16_t* __restrict__ x, int M, int K,
         }
 #pragma unroll
         for (int c = 0; c < 4; ++c)
-            *(uint4*)(stage + col_tile_offset(cg * 8 + half * 4 + c, rs * kHold)) =
+            *(uint4*)(stage + col_tile_offset(cg * 8 + half * 4 + c, rs * C::H)) =
                 make_uint4(col[c][0], col[c][1], col[c][2], col[c][3]);
     }
     __syncthreads();
@@ -933,8 +1019,8 @@ void group_quant_col_blocks_kernel(const uint16_t* __restrict__ x, int M, int K,
     const int hi = t.r1 - a;
     const bool aligned16 = (M & 15) == 0;
     const int64_t col0 = (int64_t)s * C::W;
-    for (int it = 0; it < (C::W * 8) / kTThreads; ++it) {
-        const int sid = (int)threadIdx.x + kTThreads * it;
+    for (int it = 0; it < (C::W * 8) / C::T; ++it) {
+        const int sid = (int)threadIdx.x + C::T * it;
         const int cc = sid >> 3, seg = sid & 7;
         if (col0 + cc >= K) continue;
         const int rb = seg * 16;
@@ -942,7 +1028,7 @@ void group_quant_col_blocks_kernel(const uint16_t* __restrict__ x, int M, int K,
         const uint4 val = *(const uint4*)(stage + col_tile_offset(cc, rb));
         uint8_t* dst = q + (col0 + cc) * (int64_t)M + a + rb;
         if (aligned16 && rb + 16 <= hi) {
-            *(uint4*)dst = val;
+            store_nt(val, (uint4*)dst);
         } else {
             store_partial16(val, dst, 0, rb + 16 < hi ? 16 : hi - rb, aligned16);
         }
@@ -954,7 +1040,7 @@ void group_quant_col_blocks_kernel(const uint16_t* __restrict__ x, int M, int K,
 // The scales of every group are final (written by the hold kernel's last
 // arrivals), so deferred tiles only re-read and quantize.
 template <int LAYOUT>
-__global__ __launch_bounds__(kTThreads)
+__global__ __launch_bounds__(TileCfg<LAYOUT>::T)
 void group_deferred_kernel(const uint16_t* __restrict__ x, int M, int K, int G, int S, Workspace ws,
                            const float* __restrict__ scales, uint8_t* __restrict__ q, int hold_limit, int nTiles)
 {
@@ -969,7 +1055,7 @@ void group_deferred_kernel(const uint16_t* __restrict__ x, int M, int K, int G, 
         if (!streamed && ws.deferred[(int64_t)j * S + s] == 0u) continue;
         const int cg = (int)threadIdx.x % C::CG, rs = (int)threadIdx.x / C::CG;
         const int k = s * C::W + cg * 8;
-        uint4 v[kHold];
+        uint4 v[C::H];
         load_tile<LAYOUT>(x, K, t, k, rs, v);
         ColScales cs;
         if (k < K)
@@ -1012,7 +1098,7 @@ static hipError_t launch_layout(const void* x, int M, int K, const int32_t* offs
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&rate_khz, hipDeviceAttributeWallClockRate, dev);
     if (e == hipSuccess)
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, group_hold_kernel<LAYOUT>, kTThreads, 0);
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, group_hold_kernel<LAYOUT>, C::T, 0);
     if (e != hipSuccess) return e;
     // Knobs (read per call): MXQ_GROUP_HOLD_TILES overrides the hold limit (0 sends every
     // group through the deferred kernel); MXQ_GROUP_WAIT_US bounds each wait (default
@@ -1046,17 +1132,17 @@ static hipError_t launch_layout(const void* x, int M, int K, const int32_t* offs
     hipLaunchKernelGGL(group_plan_kernel<C::R>, dim3(pgrid), dim3(kGThreads), 0, stream, offs, G, M, K, ws, nGS,
                        (int)nTiles, (int)slots, scales, nPartial16, nScale16);
     if (M > 0 && twopass) {
-        hipLaunchKernelGGL(group_amax_kernel<LAYOUT>, dim3((unsigned)nTiles), dim3(kTThreads), 0, stream,
+        hipLaunchKernelGGL(group_amax_kernel<LAYOUT>, dim3((unsigned)nTiles), dim3(C::T), 0, stream,
                            (const uint16_t*)x, K, G, S, ws);
         const int SF = (K + kFW - 1) / kFW;
         hipLaunchKernelGGL(group_finalize_kernel, dim3((unsigned)(G * SF)), dim3(kFThreads), 0, stream, K, SF, ws,
                            scales);
         if (LAYOUT == 1) {
             const int nBlk = (M + C::R - 1) / C::R;
-            hipLaunchKernelGGL(group_quant_col_blocks_kernel, dim3((unsigned)(nBlk * S)), dim3(kTThreads), 0, stream,
+            hipLaunchKernelGGL(group_quant_col_blocks_kernel, dim3((unsigned)(nBlk * S)), dim3(TileCfg<1>::T), 0, stream,
                                (const uint16_t*)x, M, K, G, S, ws, (const float*)scales, (uint8_t*)q);
         } else {
-            hipLaunchKernelGGL(group_quant_kernel<LAYOUT>, dim3((unsigned)nTiles), dim3(kTThreads), 0, stream,
+            hipLaunchKernelGGL(group_quant_kernel<LAYOUT>, dim3((unsigned)nTiles), dim3(C::T), 0, stream,
                                (const uint16_t*)x, M, K, G, S, ws, (const float*)scales, (uint8_t*)q);
         }
     } else if (M > 0) {
@@ -1064,12 +1150,12 @@ static hipError_t launch_layout(const void* x, int M, int K, const int32_t* offs
         // hold limit nothing is streamed, and tiles whose wait runs out finish
         // themselves, so the deferred pass is not launched at all.
         const int deferred = (int64_t)(M + C::R - 1) / C::R + 1 > hold_limit ? 1 : 0;
-        hipLaunchKernelGGL(group_hold_kernel<LAYOUT>, dim3((unsigned)nTiles), dim3(kTThreads), 0, stream,
+        hipLaunchKernelGGL(group_hold_kernel<LAYOUT>, dim3((unsigned)nTiles), dim3(C::T), 0, stream,
                            (const uint16_t*)x, M, K, G, S, SB, (int)slots, ws, scales, (uint8_t*)q, hold_limit,
                            timeout_ticks, deferred);
         if (!deferred) return hipGetLastError();
         const int dgrid = (int)(nTiles < 512 ? nTiles : 512);
-        hipLaunchKernelGGL(group_deferred_kernel<LAYOUT>, dim3((unsigned)dgrid), dim3(kTThreads), 0, stream,
+        hipLaunchKernelGGL(group_deferred_kernel<LAYOUT>, dim3((unsigned)dgrid), dim3(C::T), 0, stream,
                            (const uint16_t*)x, M, K, G, S, ws, (const float*)scales, (uint8_t*)q, hold_limit,
                            (int)nTiles);
     }

@@ -62,12 +62,6 @@ static_assert(kBM == kBN, "one row count serves both operand tiles");
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
-typedef __amdgpu_buffer_rsrc_t Rsrc;
-
-__device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
 
 // Workspace: int header[4] (header[0] = number of tiles), then int4 tiles[].
 struct Tile {
@@ -222,11 +216,6 @@ __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p)
 __device__ __forceinline__ void dma16(const v4i& srd, uint32_t lds, uint32_t voff)
 {
     asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds), "v"(voff), "s"(srd)
-                 : "memory");
-}
-__device__ __forceinline__ void dma4(const v4i& srd, uint32_t lds, uint32_t voff)
-{
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(lds), "v"(voff), "s"(srd)
                  : "memory");
 }
 
