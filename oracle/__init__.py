@@ -29,6 +29,8 @@ CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-s
 
 LAYOUT_ROW = 0
 LAYOUT_COL = 1
+RULE_FLOOR = 0
+RULE_RCEIL = 1
 
 
 def compile_source(src: str, out: str) -> str:
@@ -57,6 +59,8 @@ _SIGS = {
     "oracle_mx_decode_element": (_u16, [_u8, _u8]),
     "oracle_mx_quantize": (None, [_P, _i64, _i64, _P, _P]),
     "oracle_mx_dequantize": (None, [_P, _P, _i64, _i64, _P]),
+    "oracle_mx_quantize_ex": (None, [_P, _i64, _i64, ctypes.c_int, ctypes.c_int, _P, _P]),
+    "oracle_mx_dequantize_ex": (None, [_P, _P, _i64, _i64, ctypes.c_int, _P]),
     "oracle_group_scale_value": (_f32, [_f32]),
     "oracle_group_encode_element": (_u8, [_u16, _f32]),
     "oracle_group_scale": (None, [_P, _i64, _i64, _P, _i32, ctypes.c_int, _P, _P]),
@@ -145,6 +149,35 @@ class Oracle:
         y = np.empty((M, K), np.uint16)
         if M and K:
             self._L.oracle_mx_dequantize(_ptr(q), _ptr(s), M, K, _ptr(y))
+        return y
+
+    def mx_quantize_ex(self, x_bits, axis: int = 1, rule: int = RULE_FLOOR):
+        """MX variants: axis 1 = blocks of 32 along a row (scales (M, K/32)), axis 0 =
+        blocks of 32 rows of a column (scales (M/32, K)); rule RULE_FLOOR or RULE_RCEIL.
+        Returns (q (M, K) uint8 E4M3 in X's layout, s uint8 E8M0)."""
+        x = _as_u16(x_bits)
+        M, K = x.shape
+        if axis not in (0, 1) or rule not in (RULE_FLOOR, RULE_RCEIL):
+            raise ValueError("axis must be 0 or 1, rule RULE_FLOOR or RULE_RCEIL")
+        if (axis == 1 and K % 32) or (axis == 0 and M % 32):
+            raise ValueError("the blocked dimension must be a multiple of 32")
+        q = np.empty((M, K), np.uint8)
+        s = np.empty((M, K // 32) if axis == 1 else (M // 32, K), np.uint8)
+        if M and K:
+            self._L.oracle_mx_quantize_ex(_ptr(x), M, K, int(axis), int(rule), _ptr(q), _ptr(s))
+        return q, s
+
+    def mx_dequantize_ex(self, q, s, axis: int = 1):
+        """Inverse of mx_quantize_ex for either axis -> (M, K) uint16 bf16 bits."""
+        q = np.ascontiguousarray(q, dtype=np.uint8)
+        s = np.ascontiguousarray(s, dtype=np.uint8)
+        M, K = q.shape
+        want = (M, K // 32) if axis == 1 else (M // 32, K)
+        if axis not in (0, 1) or (axis == 1 and K % 32) or (axis == 0 and M % 32) or s.shape != want:
+            raise ValueError("scale shape does not match the axis")
+        y = np.empty((M, K), np.uint16)
+        if M and K:
+            self._L.oracle_mx_dequantize_ex(_ptr(q), _ptr(s), M, K, int(axis), _ptr(y))
         return y
 
     def group_scale(self, x_bits, group_end, layout: int = LAYOUT_ROW):

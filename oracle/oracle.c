@@ -219,6 +219,83 @@ void oracle_mx_dequantize(const uint8_t* q, const uint8_t* s, int64_t M, int64_t
             y[m * K + k] = oracle_mx_decode_element(q[m * K + k], s[m * nb + k / 32]);
 }
 
+/* ------------------------------------------------- MX variants ------------ */
+/* Two variants of the MX quantizer that the MX v1.0 definition above leaves to
+ * the user of the format, both readings of this repository (the pages name
+ * mxfp8 only):
+ *   scale rule RCEIL: the shared exponent is the smallest integer e for which
+ *     amax <= 448 * 2^e, i.e. ceil(log2(amax / 448)): the scale is rounded up
+ *     so that no element of the block exceeds 448 once scaled and nothing
+ *     saturates.  Clamped to [-127, 127] like the floor rule; amax = 0 gives
+ *     -127.
+ *   axis 0: blocks of 32 consecutive rows of one column (the layout a GEMM that
+ *     contracts over tokens needs), instead of 32 consecutive elements of a row.
+ * rule: 0 = floor (the rule above), 1 = RCEIL.  axis: 1 = along rows (K), 0 =
+ * along columns (M). */
+static int mx_shared_exponent(double amax, int rule)
+{
+    int e;
+    if (amax == 0.0) {
+        e = -127;
+    } else if (rule == 0) {
+        e = -8 + floor_log2(amax);             /* the floor rule, as mx_block_scale_code */
+    } else {
+        e = floor_log2(amax) - 9;              /* 448 * 2^e = 0.875 * 2^floor_log2 < amax */
+        while (amax > 448.0 * ldexp(1.0, e)) ++e;
+    }
+    if (e < -127) e = -127;
+    if (e > 127) e = 127;
+    return e;
+}
+
+/* Index of element i (0..31) of block (a, b): axis 1 -> row a, columns 32b..;
+ * axis 0 -> rows 32a.., column b. */
+static int64_t mx_block_index(int axis, int64_t K, int64_t a, int64_t b, int i)
+{
+    return axis == 1 ? a * K + b * 32 + i : (a * 32 + i) * K + b;
+}
+
+/* X: (M, K) bf16 bits row-major; Q: (M, K) E4M3 in the same layout as X.
+ * axis 1: K % 32 == 0, S (M, K/32) row-major, S[m][b] for columns 32b..32b+31.
+ * axis 0: M % 32 == 0, S (M/32, K) row-major, S[a][k] for rows 32a..32a+31. */
+void oracle_mx_quantize_ex(const uint16_t* x, int64_t M, int64_t K, int axis, int rule, uint8_t* q, uint8_t* s)
+{
+    const int64_t na = axis == 1 ? M : M / 32;     /* blocks: na x nb */
+    const int64_t nb = axis == 1 ? K / 32 : K;
+    double v[32];
+    for (int64_t a = 0; a < na; ++a) {
+        for (int64_t b = 0; b < nb; ++b) {
+            double amax = 0.0;
+            int finite = 1;
+            for (int i = 0; i < 32; ++i) {
+                v[i] = oracle_bf16_value(x[mx_block_index(axis, K, a, b, i)]);
+                if (!is_finite_d(v[i])) finite = 0;
+                else if (fabs(v[i]) > amax) amax = fabs(v[i]);
+            }
+            if (!finite) {
+                s[a * nb + b] = 0xFF;
+                for (int i = 0; i < 32; ++i) q[mx_block_index(axis, K, a, b, i)] = 0x7F;
+                continue;
+            }
+            const int e = mx_shared_exponent(amax, rule);
+            s[a * nb + b] = (uint8_t)(e + 127);
+            for (int i = 0; i < 32; ++i)
+                q[mx_block_index(axis, K, a, b, i)] = oracle_e4m3_encode(v[i] / ldexp(1.0, e));
+        }
+    }
+}
+
+/* Inverse of oracle_mx_quantize_ex for either axis: each element is decoded
+ * with its own block's scale exactly as oracle_mx_decode_element does. */
+void oracle_mx_dequantize_ex(const uint8_t* q, const uint8_t* s, int64_t M, int64_t K, int axis, uint16_t* y)
+{
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t k = 0; k < K; ++k) {
+            const uint8_t c = axis == 1 ? s[m * (K / 32) + k / 32] : s[(m / 32) * K + k];
+            y[m * K + k] = oracle_mx_decode_element(q[m * K + k], c);
+        }
+}
+
 /* ------------------------------------------------------ group scaling ----- */
 
 /* binary32 helpers: every operation here is one correctly rounded IEEE op. */

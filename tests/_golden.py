@@ -82,9 +82,9 @@ def _fields(line):
     return head[0], head[1], fields
 
 
-def load_mx_cases():
+def load_mx_cases(name="mx_worked_blocks.txt"):
     blocks, decodes = [], []
-    with open(os.path.join(GOLDEN, "mx_worked_blocks.txt")) as f:
+    with open(os.path.join(GOLDEN, name)) as f:
         for line in f:
             line = line.strip()
             if not line or line.startswith("#"):

@@ -236,6 +236,82 @@ def check_mx_row_block_layout(o, seed=9):
             assert np.array_equal(yb[0], y[m, 32 * b:32 * b + 32])
 
 
+# ---------------------------------------------------------- MX variants ---
+RULE_RCEIL = 1
+
+
+def check_mx_rceil_worked_blocks(o):
+    """Hand-worked RCEIL blocks (tests/golden/mx_rceil_blocks.txt), as rows and as columns."""
+    blocks, _ = _golden.load_mx_cases("mx_rceil_blocks.txt")
+    for b in blocks:
+        x = np.array([b["x"]], dtype=np.uint16)
+        q, s = o.mx_quantize_ex(x, axis=1, rule=RULE_RCEIL)
+        assert s[0, 0] == b["s"], (b["name"], hex(int(s[0, 0])), hex(b["s"]))
+        assert list(q[0]) == b["q"], (b["name"], [hex(int(v)) for v in q[0]])
+        assert list(o.mx_dequantize_ex(q, s, axis=1)[0]) == b["y"], b["name"]
+        q0, s0 = o.mx_quantize_ex(np.ascontiguousarray(x.T), axis=0, rule=RULE_RCEIL)
+        assert s0.shape == (1, 1) and s0[0, 0] == b["s"] and list(q0[:, 0]) == b["q"], b["name"]
+        assert list(o.mx_dequantize_ex(q0, s0, axis=0)[:, 0]) == b["y"], b["name"]
+
+
+def check_mx_rceil_vs_division(o, nblocks=20000, seed=15):
+    """RCEIL code = ceil(log2(amax / 448)) + 127 with the quotient from numpy's binary64
+    division and the ceiling read off frexp (a quotient of bf16 amax by 448 is either an
+    exact power of two or at least 2^-9 away from one in relative terms); the codes are
+    the element-wise MX encoder's under that scale; nothing saturates."""
+    rng = np.random.default_rng(seed)
+    x = _random_blocks(rng, nblocks)
+    q, s = o.mx_quantize_ex(x, axis=1, rule=RULE_RCEIL)
+    codes = s[:, 0].astype(np.int64)
+    amax = np.abs(_f32_of_bf16(x).astype(np.float64)).max(axis=1)
+    nz = amax > 0
+    f, e = np.frexp(amax[nz] / 448.0)
+    ceil_log2 = np.where(f == 0.5, e - 1, e)
+    want = np.zeros(amax.shape, np.int64)
+    want[nz] = np.clip(ceil_log2 + 127, 0, 254)
+    assert np.array_equal(codes, want)
+    assert np.array_equal(q.ravel(), o.mx_encode_elements(x.ravel(), np.repeat(s[:, 0], 32)))
+    dec = np.abs(torch.from_numpy(q.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy())
+    assert dec.max() <= 448.0
+    # for blocks whose code is not clamped, the scaled maximum lies in (224, 448] and encodes in [224, 448]
+    free = nz & (want > 0)
+    bmax = dec[free].max(axis=1)
+    assert np.all((bmax >= 224) & (bmax <= 448))
+    # against the floor rule: the same code, or one more exactly when amax's bf16 mantissa
+    # exceeds 0x60 (1.75) -- read off the bit patterns, for blocks neither rule clamps
+    _, sf = o.mx_quantize(x)
+    amax_bits = (x & 0x7FFF).max(axis=1).astype(np.int64)
+    unclamped = (sf[:, 0] > 0) & (amax_bits < 0x7F80)
+    inc = ((amax_bits & 0x7F) > 0x60).astype(np.int64)
+    assert np.array_equal(codes[unclamped], sf[unclamped, 0].astype(np.int64) + inc[unclamped])
+
+
+def check_mx_axis0_is_transpose(o, seed=16):
+    """Blocks along dim 0 are the row blocks of the transpose, for both rules; the
+    floor rule along dim 1 is the MX quantizer pinned above; one 32 x 1 block at a
+    time gives the same bytes as the whole call."""
+    rng = np.random.default_rng(seed)
+    M, K = 64, 96
+    x = _random_blocks(rng, M * K // 32).reshape(M, K)
+    for rule in (0, RULE_RCEIL):
+        q0, s0 = o.mx_quantize_ex(x, axis=0, rule=rule)
+        q1, s1 = o.mx_quantize_ex(np.ascontiguousarray(x.T), axis=1, rule=rule)
+        assert s0.shape == (M // 32, K)
+        assert np.array_equal(q0, q1.T) and np.array_equal(s0, s1.T)
+        y0 = o.mx_dequantize_ex(q0, s0, axis=0)
+        y1 = o.mx_dequantize_ex(q1, s1, axis=1)
+        assert np.array_equal(y0, y1.T)
+    qf, sf = o.mx_quantize_ex(x, axis=1, rule=0)
+    qr, sr = o.mx_quantize(x)
+    assert np.array_equal(qf, qr) and np.array_equal(sf, sr)
+    assert np.array_equal(o.mx_dequantize_ex(qr, sr, axis=1), o.mx_dequantize(qr, sr))
+    q0, s0 = o.mx_quantize_ex(x, axis=0, rule=RULE_RCEIL)
+    for a in (0, 1):
+        for k in (0, 5, K - 1):
+            qb, sb = o.mx_quantize_ex(np.ascontiguousarray(x[32 * a:32 * a + 32, k:k + 1]), axis=0, rule=RULE_RCEIL)
+            assert sb[0, 0] == s0[a, k] and np.array_equal(qb[:, 0], q0[32 * a:32 * a + 32, k])
+
+
 # -------------------------------------------------------- group scaling ---
 def check_group_worked(o):
     for c in _golden.load_group_cases():
@@ -471,6 +547,7 @@ FAST_CHECKS = [
     check_group_offsets_clamped, check_transpose,
     check_grouped_mm_vs_torch, check_grouped_mm_closed_form, check_grouped_mm_block_scales,
     check_grouped_mm_nan,
+    check_mx_rceil_worked_blocks, check_mx_rceil_vs_division, check_mx_axis0_is_transpose,
 ]
 
 

@@ -40,6 +40,13 @@ MUTATIONS = [
     ("mm_group_end_inclusive", "if (r >= start && r < end) { grp = g; break; }",
      "if (r >= start && r <= end) { grp = g; break; }"),
     ("transpose_identity", "out[j * R + i] = in[i * C + j];", "out[i * C + j] = in[i * C + j];"),
+    ("rceil_boundary_inclusive", "while (amax > 448.0 * ldexp(1.0, e)) ++e;", "while (amax >= 448.0 * ldexp(1.0, e)) ++e;"),
+    ("rceil_wrong_max", "while (amax > 448.0 * ldexp(1.0, e)) ++e;", "while (amax > 480.0 * ldexp(1.0, e)) ++e;"),
+    ("rceil_is_floor", "} else if (rule == 0) {", "} else if (rule >= 0) {"),
+    ("rceil_floor_emax", "e = -8 + floor_log2(amax);", "e = -7 + floor_log2(amax);"),
+    ("axis0_block_rows", "(a * 32 + i) * K + b;", "(a + i) * K + b;"),
+    ("axis0_dequant_scale_row", "s[(m / 32) * K + k]", "s[(m % 32) * K + k]"),
+    ("axis1_ex_dequant_scale", "s[m * (K / 32) + k / 32]", "s[m * (K / 32) + k % 32]"),
 ]
 
 
