@@ -48,6 +48,7 @@ const char* mxq_status_string(int status)
     case MXQ_ERR_HIP: return "MXQ_ERR_HIP: a HIP runtime call failed";
     case MXQ_ERR_NOT_IMPLEMENTED: return "MXQ_ERR_NOT_IMPLEMENTED";
     case MXQ_ERR_DTYPE: return "MXQ_ERR_DTYPE: unknown output data type";
+    case MXQ_ERR_RULE: return "MXQ_ERR_RULE: unknown scale rule";
     default: return "unknown mxq_status";
     }
 }
@@ -62,7 +63,47 @@ mxq_status mxq_quantize_mx(const void* x_bf16, int64_t M, int64_t K, void* q_e4m
     if (M == 0 || K == 0) return MXQ_OK;
     if (!x_bf16 || !q_e4m3 || !s_e8m0) return MXQ_ERR_NULL;
     if (!aligned16(x_bf16) || !aligned16(q_e4m3) || !aligned16(s_e8m0)) return MXQ_ERR_ALIGN;
-    return hip_status(mxq::launch_mx_quantize(x_bf16, M, K, q_e4m3, s_e8m0, (hipStream_t)stream));
+    return hip_status(mxq::launch_mx_quantize(x_bf16, M, K, q_e4m3, s_e8m0, false, (hipStream_t)stream));
+}
+
+// Sizes of the MX variants: axis 1 as the plain codec; axis 0 needs whole 32-row
+// blocks, 4-column lanes, and keeps its buffer resources (32 rows) and grid in range.
+static mxq_status check_mx_ex(int64_t M, int64_t K, int axis)
+{
+    mxq_status st = check_2d(M, K);
+    if (st != MXQ_OK) return st;
+    if (axis != 0 && axis != 1) return MXQ_ERR_LAYOUT;
+    if (axis == 1) return K % 32 == 0 ? MXQ_OK : MXQ_ERR_SHAPE;
+    if (M % 32 != 0 || K % 4 != 0 || K > ((int64_t)1 << 24)) return MXQ_ERR_SHAPE;
+    if ((M / 32) * ((K + 1023) / 1024) >= ((int64_t)1 << 31)) return MXQ_ERR_SHAPE;
+    return MXQ_OK;
+}
+
+mxq_status mxq_quantize_mx_ex(const void* x_bf16, int64_t M, int64_t K, int axis, int rule, void* q_e4m3,
+                              void* s_e8m0, void* stream)
+{
+    mxq_status st = check_mx_ex(M, K, axis);
+    if (st != MXQ_OK) return st;
+    if (rule != MXQ_SCALE_FLOOR && rule != MXQ_SCALE_RCEIL) return MXQ_ERR_RULE;
+    if (M == 0 || K == 0) return MXQ_OK;
+    if (!x_bf16 || !q_e4m3 || !s_e8m0) return MXQ_ERR_NULL;
+    if (!aligned16(x_bf16) || !aligned16(q_e4m3) || !aligned16(s_e8m0)) return MXQ_ERR_ALIGN;
+    const bool rceil = rule == MXQ_SCALE_RCEIL;
+    if (axis == 1)
+        return hip_status(mxq::launch_mx_quantize(x_bf16, M, K, q_e4m3, s_e8m0, rceil, (hipStream_t)stream));
+    return hip_status(mxq::launch_mx_quantize_dim0(x_bf16, M, K, q_e4m3, s_e8m0, rceil, (hipStream_t)stream));
+}
+
+mxq_status mxq_dequantize_mx_ex(const void* q_e4m3, const void* s_e8m0, int64_t M, int64_t K, int axis,
+                                void* y_bf16, void* stream)
+{
+    mxq_status st = check_mx_ex(M, K, axis);
+    if (st != MXQ_OK) return st;
+    if (M == 0 || K == 0) return MXQ_OK;
+    if (!q_e4m3 || !s_e8m0 || !y_bf16) return MXQ_ERR_NULL;
+    if (!aligned16(q_e4m3) || !aligned16(s_e8m0) || !aligned16(y_bf16)) return MXQ_ERR_ALIGN;
+    if (axis == 1) return hip_status(mxq::launch_mx_dequantize(q_e4m3, s_e8m0, M, K, y_bf16, (hipStream_t)stream));
+    return hip_status(mxq::launch_mx_dequantize_dim0(q_e4m3, s_e8m0, M, K, y_bf16, (hipStream_t)stream));
 }
 
 mxq_status mxq_dequantize_mx(const void* q_e4m3, const void* s_e8m0, int64_t M, int64_t K, void* y_bf16,

@@ -64,6 +64,20 @@ __device__ __forceinline__ float pow2_from_biased(uint32_t e)
     return __uint_as_float(e ? (e << 23) : 0x00400000u);
 }
 
+// E8M0 code of a block whose largest |bf16| bit pattern is amax (finite).  E is
+// amax's biased exponent, so floor(log2 amax) = E - 127 for normal amax.
+//   floor rule (OCP MX v1.0): floor(log2 amax) - 8, i.e. code E - 8.
+//   RCEIL: the smallest e with amax <= 448 * 2^e.  448 * 2^(E-127-8) is 1.75 *
+//     2^(E-127), so e is E - 135 when amax's significand is at most 1.75
+//     (mantissa bits <= 0x60) and one more otherwise: code E - 8 + (m > 0x60).
+// Both clamp at code 0 (amax zero, subnormal or below the smallest scale).
+template <bool RCEIL>
+__device__ __forceinline__ uint32_t mx_scale_code(uint32_t amax)
+{
+    const uint32_t E = (amax >> 7) + (RCEIL && (amax & 0x7Fu) > 0x60u ? 1u : 0u);
+    return E > 8u ? E - 8u : 0u;
+}
+
 __device__ __forceinline__ float bf16_lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 

@@ -8,7 +8,11 @@
 
 namespace mxq {
 
-hipError_t launch_mx_quantize(const void* x, int64_t M, int64_t K, void* q, void* s, hipStream_t stream);
+hipError_t launch_mx_quantize(const void* x, int64_t M, int64_t K, void* q, void* s, bool rceil, hipStream_t stream);
+hipError_t launch_mx_quantize_dim0(const void* x, int64_t M, int64_t K, void* q, void* s, bool rceil,
+                                   hipStream_t stream);
+hipError_t launch_mx_dequantize_dim0(const void* q, const void* s, int64_t M, int64_t K, void* y,
+                                     hipStream_t stream);
 hipError_t launch_mx_dequantize(const void* q, const void* s, int64_t M, int64_t K, void* y, hipStream_t stream);
 
 bool group_scale_sizes_ok(int64_t M, int64_t K, int64_t G);

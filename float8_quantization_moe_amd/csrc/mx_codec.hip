@@ -23,6 +23,8 @@ constexpr int kCodecThreads = 256;
 constexpr int kCodecUnroll = 4;   // independent 16-byte loads in flight per lane
 
 // One 16-byte chunk (8 bf16) -> 8 E4M3 codes; returns the block's E8M0 code in *scode.
+// RCEIL selects the round-up scale rule (see mx_scale_code).
+template <bool RCEIL>
 __device__ __forceinline__ uint2 quantize_chunk(uint4 v, uint32_t* scode)
 {
     const uint32_t m0 = v.x & 0x7FFF7FFFu, m1 = v.y & 0x7FFF7FFFu;
@@ -31,10 +33,7 @@ __device__ __forceinline__ uint2 quantize_chunk(uint4 v, uint32_t* scode)
     uint32_t amax = (pm & 0xFFFFu) > (pm >> 16) ? (pm & 0xFFFFu) : (pm >> 16);
     amax = quad_max_u32(amax);
 
-    // E8M0 code = floor(log2 amax) - 8 + 127 = (biased bf16 exponent of amax) - 8,
-    // clamped at 0 (amax zero or subnormal, or below 2^-119).
-    const uint32_t E = amax >> 7;
-    const uint32_t code = E > 8u ? E - 8u : 0u;
+    const uint32_t code = mx_scale_code<RCEIL>(amax);
     if (amax >= 0x7F80u) {                       // Inf or NaN in the block
         *scode = 0xFFu;
         return make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu);
@@ -56,6 +55,7 @@ __device__ __forceinline__ uint2 quantize_chunk(uint4 v, uint32_t* scode)
     return make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
 }
 
+template <bool RCEIL>
 __global__ __launch_bounds__(kCodecThreads)
 void mx_quantize_kernel(const uint4* __restrict__ x, uint2* __restrict__ q, uint8_t* __restrict__ s,
                         int64_t nchunks)
@@ -73,7 +73,7 @@ void mx_quantize_kernel(const uint4* __restrict__ x, uint2* __restrict__ q, uint
         for (int u = 0; u < kCodecUnroll; ++u) {
             const int64_t c = base + (int64_t)u * kCodecThreads;
             uint32_t code;
-            const uint2 out = quantize_chunk(v[u], &code);   // whole quads are in or out of range
+            const uint2 out = quantize_chunk<RCEIL>(v[u], &code);   // whole quads are in or out of range
             if (c < nchunks) {
                 store_nt(out, q + c);
                 if ((threadIdx.x & 3) == 0) s[c >> 2] = (uint8_t)code;
@@ -141,11 +141,15 @@ static unsigned codec_grid(int64_t nchunks)
     return (unsigned)(blocks < cap ? blocks : cap);
 }
 
-hipError_t launch_mx_quantize(const void* x, int64_t M, int64_t K, void* q, void* s, hipStream_t stream)
+hipError_t launch_mx_quantize(const void* x, int64_t M, int64_t K, void* q, void* s, bool rceil, hipStream_t stream)
 {
     const int64_t nchunks = M * K / 8;
-    hipLaunchKernelGGL(mx_quantize_kernel, dim3(codec_grid(nchunks)), dim3(kCodecThreads), 0, stream,
-                       (const uint4*)x, (uint2*)q, (uint8_t*)s, nchunks);
+    if (rceil)
+        hipLaunchKernelGGL(mx_quantize_kernel<true>, dim3(codec_grid(nchunks)), dim3(kCodecThreads), 0, stream,
+                           (const uint4*)x, (uint2*)q, (uint8_t*)s, nchunks);
+    else
+        hipLaunchKernelGGL(mx_quantize_kernel<false>, dim3(codec_grid(nchunks)), dim3(kCodecThreads), 0, stream,
+                           (const uint4*)x, (uint2*)q, (uint8_t*)s, nchunks);
     return hipGetLastError();
 }
 

@@ -27,12 +27,16 @@ MXQ_LAYOUT_COL = 1
 MXQ_OK = 0
 MXQ_ERR_NULL, MXQ_ERR_SHAPE, MXQ_ERR_ALIGN, MXQ_ERR_LAYOUT, MXQ_ERR_WORKSPACE, MXQ_ERR_HIP = 1, 2, 3, 4, 5, 6
 MXQ_ERR_DTYPE = 8
+MXQ_ERR_RULE = 9
 MXQ_OUT_BF16 = 0
 MXQ_OUT_F32 = 1
+MXQ_SCALE_FLOOR = 0
+MXQ_SCALE_RCEIL = 1
 
 EXPORTED = ("mxq_abi_version", "mxq_status_string", "mxq_last_hip_error", "mxq_quantize_mx",
             "mxq_dequantize_mx", "mxq_group_scale_workspace_bytes", "mxq_group_scale_fp8",
-            "mxq_transpose_u8", "mxq_grouped_mm_workspace_bytes", "mxq_scaled_grouped_mm")
+            "mxq_transpose_u8", "mxq_grouped_mm_workspace_bytes", "mxq_scaled_grouped_mm",
+            "mxq_quantize_mx_ex", "mxq_dequantize_mx_ex")
 
 
 class MxqError(RuntimeError):
@@ -66,6 +70,10 @@ def lib() -> ctypes.CDLL:
         L.mxq_quantize_mx.argtypes = [P, i64, i64, P, P, P]
         L.mxq_dequantize_mx.restype = ctypes.c_int
         L.mxq_dequantize_mx.argtypes = [P, P, i64, i64, P, P]
+        L.mxq_quantize_mx_ex.restype = ctypes.c_int
+        L.mxq_quantize_mx_ex.argtypes = [P, i64, i64, ctypes.c_int, ctypes.c_int, P, P, P]
+        L.mxq_dequantize_mx_ex.restype = ctypes.c_int
+        L.mxq_dequantize_mx_ex.argtypes = [P, P, i64, i64, ctypes.c_int, P, P]
         L.mxq_group_scale_workspace_bytes.restype = sz
         L.mxq_group_scale_workspace_bytes.argtypes = [i64, i64, i32]
         L.mxq_group_scale_fp8.restype = ctypes.c_int
@@ -131,6 +139,38 @@ def mxq_dequantize_mx(q: torch.Tensor, s: torch.Tensor, y: torch.Tensor, stream=
     ps = _dev(s, "s", torch.uint8, M * (K // 32) if K % 32 == 0 else None)
     py = _dev(y, "y", torch.bfloat16)
     _check(lib().mxq_dequantize_mx(pq, ps, M, K, py, _stream(stream)), "mxq_dequantize_mx")
+
+
+def _mx_scale_numel(M: int, K: int, axis: int):
+    if axis == 1:
+        return M * (K // 32) if K % 32 == 0 else None
+    if axis == 0:
+        return (M // 32) * K if M % 32 == 0 else None
+    return None
+
+
+def mxq_quantize_mx_ex(x: torch.Tensor, axis: int, rule: int, q: torch.Tensor, s: torch.Tensor,
+                       stream=None) -> None:
+    """MX variants: x (M, K) bf16 -> q (M, K) uint8 E4M3 and s E8M0 codes, (M, K/32) for
+    axis 1 or (M/32, K) for axis 0; rule MXQ_SCALE_FLOOR or MXQ_SCALE_RCEIL."""
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D (M, K)")
+    M, K = x.shape
+    px = _dev(x, "x", torch.bfloat16)
+    pq = _dev(q, "q", torch.uint8, M * K)
+    ps = _dev(s, "s", torch.uint8, _mx_scale_numel(M, K, axis))
+    _check(lib().mxq_quantize_mx_ex(px, M, K, int(axis), int(rule), pq, ps, _stream(stream)), "mxq_quantize_mx_ex")
+
+
+def mxq_dequantize_mx_ex(q: torch.Tensor, s: torch.Tensor, axis: int, y: torch.Tensor, stream=None) -> None:
+    """Inverse of mxq_quantize_mx_ex for either axis -> y (M, K) bf16."""
+    if y.dim() != 2:
+        raise ValueError("y must be 2-D (M, K)")
+    M, K = y.shape
+    pq = _dev(q, "q", torch.uint8, M * K)
+    ps = _dev(s, "s", torch.uint8, _mx_scale_numel(M, K, axis))
+    py = _dev(y, "y", torch.bfloat16)
+    _check(lib().mxq_dequantize_mx_ex(pq, ps, M, K, int(axis), py, _stream(stream)), "mxq_dequantize_mx_ex")
 
 
 def mxq_group_scale_workspace_bytes(M: int, K: int, G: int) -> int:

@@ -59,7 +59,8 @@ typedef enum mxq_status {
     MXQ_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required          */
     MXQ_ERR_HIP = 6,         /* a HIP runtime call failed (launch, device query)    */
     MXQ_ERR_NOT_IMPLEMENTED = 7,
-    MXQ_ERR_DTYPE = 8        /* unknown mxq_out_dtype value                         */
+    MXQ_ERR_DTYPE = 8,       /* unknown mxq_out_dtype value                         */
+    MXQ_ERR_RULE = 9         /* unknown mxq_scale_rule value                        */
 } mxq_status;
 
 typedef enum mxq_layout {
@@ -68,6 +69,13 @@ typedef enum mxq_layout {
                                 (K, M) row-major operand of a GEMM that contracts
                                 over the tokens of each group                        */
 } mxq_layout;
+
+typedef enum mxq_scale_rule {
+    MXQ_SCALE_FLOOR = 0,     /* OCP MX v1.0: shared exponent floor(log2 amax) - 8;
+                                elements above 448 once scaled saturate             */
+    MXQ_SCALE_RCEIL = 1      /* round the scale up: the smallest e with
+                                amax <= 448 * 2^e, so nothing saturates             */
+} mxq_scale_rule;
 
 typedef enum mxq_out_dtype {
     MXQ_OUT_BF16 = 0,        /* bfloat16, rounded to nearest even from the fp32 sum  */
@@ -124,6 +132,37 @@ mxq_status mxq_quantize_mx(const void* x_bf16, int64_t M, int64_t K,
  */
 mxq_status mxq_dequantize_mx(const void* q_e4m3, const void* s_e8m0, int64_t M, int64_t K,
                              void* y_bf16, void* stream);
+
+/*
+ * MXFP8 variants: the scale rule and the blocking axis.
+ * Source: "[mxfp8 MoE training] Support mxfp8 all to all in expert parallel",
+ * Summary (the e4m3 + e8m0 encoding of the payload).  The pages name mxfp8
+ * only; the two choices below are what the format leaves to its user: how the
+ * shared exponent is rounded, and along which dimension 32 elements share it
+ * (blocks along the token dimension are what a GEMM contracting over tokens,
+ * the weight gradient of a MoE layer, consumes).
+ *
+ *   axis 1: blocks of 32 consecutive elements of a row; s_e8m0 is (M, K/32)
+ *           row-major exactly as for mxq_quantize_mx.  Requires K % 32 == 0.
+ *   axis 0: blocks of 32 consecutive rows of one column; s_e8m0 is (M/32, K)
+ *           row-major, S[a][k] covering x[32a .. 32a+31][k].  Requires
+ *           M % 32 == 0, K % 4 == 0, K <= 2^24 and (M/32)*ceil(K/1024) < 2^31.
+ *   Any other axis value: MXQ_ERR_LAYOUT.
+ *   q_e4m3 is (M, K) row-major (X's layout) for both axes.
+ *   rule: MXQ_SCALE_FLOOR (the rule of mxq_quantize_mx) or MXQ_SCALE_RCEIL
+ *         (scale code = E - 8 + (mantissa of amax > 1.75), i.e. the smallest
+ *         power-of-two scale with amax / scale <= 448), both clamped to
+ *         [0, 254]; anything else: MXQ_ERR_RULE.  Rounding, signs, NaN/Inf
+ *         blocks (scale 0xFF, codes 0x7F) as for mxq_quantize_mx.
+ * mxq_quantize_mx_ex(x, M, K, 1, MXQ_SCALE_FLOOR, ...) produces the same bytes as
+ * mxq_quantize_mx.  mxq_dequantize_mx_ex decodes either axis exactly as
+ * mxq_dequantize_mx (the rule does not change decoding).  Shape and size errors
+ * as for mxq_quantize_mx; M == 0 or K == 0 is a no-op.
+ */
+mxq_status mxq_quantize_mx_ex(const void* x_bf16, int64_t M, int64_t K, int axis, int rule,
+                              void* q_e4m3, void* s_e8m0, void* stream);
+mxq_status mxq_dequantize_mx_ex(const void* q_e4m3, const void* s_e8m0, int64_t M, int64_t K,
+                                int axis, void* y_bf16, void* stream);
 
 /*
  * Bytes of device workspace mxq_group_scale_fp8 needs for these sizes (0 for

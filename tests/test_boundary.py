@@ -29,7 +29,8 @@ def test_header_declares_the_entry_points():
     names = _declared()
     for n in ("mxq_quantize_mx", "mxq_dequantize_mx", "mxq_group_scale_fp8",
               "mxq_group_scale_workspace_bytes", "mxq_transpose_u8", "mxq_abi_version",
-              "mxq_grouped_mm_workspace_bytes", "mxq_scaled_grouped_mm"):
+              "mxq_grouped_mm_workspace_bytes", "mxq_scaled_grouped_mm", "mxq_quantize_mx_ex",
+              "mxq_dequantize_mx_ex"):
         assert n in names
 
 
@@ -43,7 +44,7 @@ def test_every_declared_symbol_is_exported(L):
 
 def test_abi_version_and_status_strings(L):
     assert L.mxq_abi_version() == 1
-    for code in range(0, 9):
+    for code in range(0, 10):
         assert L.mxq_status_string(code).startswith(b"MXQ_")
     assert L.mxq_status_string(99) == b"unknown mxq_status"
     assert L.mxq_last_hip_error() == 0
@@ -75,6 +76,29 @@ def test_dequantize_mx_argument_errors(L):
     assert L.mxq_dequantize_mx(A, A, 4, 32, 0, S) == 1
     assert L.mxq_dequantize_mx(A, A + 4, 4, 32, A, S) == 3
     assert L.mxq_dequantize_mx(0, 0, 0, 64, 0, S) == 0
+
+
+def test_mx_variant_argument_errors(L):
+    S = 0
+    q, d = L.mxq_quantize_mx_ex, L.mxq_dequantize_mx_ex
+    assert q(A, 64, 64, 2, 0, A, A, S) == 4                    # unknown axis
+    assert q(A, 64, 64, -1, 0, A, A, S) == 4
+    assert q(A, 64, 64, 1, 2, A, A, S) == 9                    # unknown rule
+    assert q(A, 64, 64, 0, -1, A, A, S) == 9
+    assert q(A, 4, 48, 1, 1, A, A, S) == 2                     # axis 1: K % 32
+    assert q(A, 48, 64, 0, 1, A, A, S) == 2                    # axis 0: M % 32
+    assert q(A, 64, 6, 0, 0, A, A, S) == 2                     # axis 0: K % 4
+    assert q(A, 32, (1 << 24) + 4, 0, 0, A, A, S) == 2         # axis 0: K too large
+    assert q(A, 1 << 36, 1024, 0, 0, A, A, S) == 2             # axis 0: grid too large
+    assert q(0, 64, 64, 0, 1, A, A, S) == 1                    # null
+    assert q(A, 64, 64, 0, 1, A, 0, S) == 1
+    assert q(A, 64, 64, 0, 1, A + 4, A, S) == 3                # misaligned
+    assert q(0, 0, 64, 0, 1, 0, 0, S) == 0                     # empty: no-op
+    assert d(A, A, 64, 64, 3, A, S) == 4
+    assert d(A, A, 40, 64, 0, A, S) == 2
+    assert d(A, A, 64, 64, 0, 0, S) == 1
+    assert d(A, A + 8, 64, 64, 0, A, S) == 3
+    assert d(0, 0, 64, 0, 0, 0, S) == 0
 
 
 def test_group_scale_argument_errors(L):
