@@ -367,6 +367,31 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         per_call_us[c] = e0.elapsed_time(e1) * 1e3 / reps
+    # Variants of the path's calls (the NEXT rows), each alone on the same rotated
+    # buffers and shapes; reported beside the step, not part of `value`.
+    FLOOR, RCEIL = mxq.MXQ_SCALE_FLOOR, mxq.MXQ_SCALE_RCEIL
+    s_dim0 = lambda b: b.s1.view(M1 // 32, K1)      # (M/32, K) scales: the same byte count as (M, K/32)
+    variant_calls = [
+        ("mx_quantize_rows_rceil", mx_bytes(M1, K1), lambda b: mxq.mxq_quantize_mx_ex(b.x1, 1, RCEIL, b.q1, b.s1, stream)),
+        ("mx_quantize_cols_floor", mx_bytes(M1, K1), lambda b: mxq.mxq_quantize_mx_ex(b.x1, 0, FLOOR, b.q1, s_dim0(b), stream)),
+        ("mx_quantize_cols_rceil", mx_bytes(M1, K1), lambda b: mxq.mxq_quantize_mx_ex(b.x1, 0, RCEIL, b.q1, s_dim0(b), stream)),
+        ("mx_dequantize_cols", mx_bytes(M1, K1), lambda b: mxq.mxq_dequantize_mx_ex(b.q1, s_dim0(b), 0, b.y1, stream)),
+    ]
+    variants = {}
+    for name, nbytes, fn in variant_calls:
+        for b in sets:
+            fn(b)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for r in range(reps):
+            fn(sets[r % len(sets)])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        variants[name] = {"avg_us": round(us, 2), "algorithmic_bytes": nbytes, "GBps": round(nbytes / (us * 1e3), 1),
+                          "frac_of_peak": round(nbytes / (us * 1e3) / HBM_PEAK_GBPS, 4),
+                          "shape": [M1, K1]}
     for i in range(2):
         step(i)
     torch.cuda.synchronize()
@@ -495,6 +520,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu_baseline,
         "kernels": kernels,
+        "variants": variants,
         "grouped_mm": grouped_mm,
         "kernels_method": "each call alone, back to back over the rotated buffer sets, events at both ends",
         "copy_ceiling_GBps": round(copy_gbps, 1),
