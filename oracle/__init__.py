@@ -31,6 +31,8 @@ LAYOUT_ROW = 0
 LAYOUT_COL = 1
 RULE_FLOOR = 0
 RULE_RCEIL = 1
+GROUP_POW2_SCALE = 1
+GROUP_INVERSE_SCALE = 2
 
 
 def compile_source(src: str, out: str) -> str:
@@ -64,6 +66,7 @@ _SIGS = {
     "oracle_group_scale_value": (_f32, [_f32]),
     "oracle_group_encode_element": (_u8, [_u16, _f32]),
     "oracle_group_scale": (None, [_P, _i64, _i64, _P, _i32, ctypes.c_int, _P, _P]),
+    "oracle_group_scale_ex": (None, [_P, _i64, _i64, _P, _i32, ctypes.c_int, ctypes.c_int, _P, _P]),
     "oracle_transpose_u8": (None, [_P, _i64, _i64, _P]),
     "oracle_mx_encode_elements": (None, [_P, _P, _i64, _P]),
     "oracle_mx_decode_elements": (None, [_P, _P, _i64, _P]),
@@ -194,6 +197,22 @@ class Oracle:
         q = np.empty((M, K) if layout == LAYOUT_ROW else (K, M), np.uint8)
         scales = np.empty((G, K), np.float32)
         self._L.oracle_group_scale(_ptr(x), M, K, _ptr(ends), G, int(layout), _ptr(q), _ptr(scales))
+        return q, scales
+
+    def group_scale_ex(self, x_bits, group_end, layout: int = LAYOUT_ROW, flags: int = 0):
+        """Group scaling with the variant flags GROUP_POW2_SCALE (multiplier rounded down
+        to a power of two) and GROUP_INVERSE_SCALE (1/s stored instead of s)."""
+        x = _as_u16(x_bits)
+        M, K = x.shape
+        ends = np.ascontiguousarray(np.asarray(group_end, dtype=np.int32))
+        G = int(ends.shape[0])
+        if G < 1:
+            raise ValueError("need at least one group")
+        if flags & ~(GROUP_POW2_SCALE | GROUP_INVERSE_SCALE):
+            raise ValueError("unknown flag")
+        q = np.empty((M, K) if layout == LAYOUT_ROW else (K, M), np.uint8)
+        scales = np.empty((G, K), np.float32)
+        self._L.oracle_group_scale_ex(_ptr(x), M, K, _ptr(ends), G, int(layout), int(flags), _ptr(q), _ptr(scales))
         return q, scales
 
     def transpose_u8(self, a):

@@ -367,6 +367,67 @@ void oracle_group_scale(const uint16_t* x, int64_t M, int64_t K,
         }
 }
 
+/* Group-scaling variants (readings of this repository; the pages fix neither):
+ *   flag 1, power-of-two scales: the multiplier s is rounded down to a power of
+ *     two, s' = 2^floor(log2 s), so that amax * s' <= 448 still holds and the
+ *     scaled product x * s' is exact; q = e4m3(binary32(x * s')).
+ *   flag 2, inverse scales: the stored scale is the dequantization factor
+ *     1 / s (one binary32 division) instead of the multiplier; the codes are
+ *     those of the multiplier convention.
+ * Both flags may be combined; NaN columns store NaN either way. */
+static float group_pow2_floor(float s)
+{
+    int e;
+    (void)frexpf(s, &e);                       /* s = f * 2^e, f in [0.5, 1) */
+    return ldexpf(1.0f, e - 1);
+}
+
+void oracle_group_scale_ex(const uint16_t* x, int64_t M, int64_t K,
+                           const int32_t* group_end, int32_t G, int layout, int flags,
+                           uint8_t* q, float* scales)
+{
+    int64_t start = 0;
+    for (int32_t g = 0; g < G; ++g) {
+        int64_t end = group_end[g];
+        if (end < start) {
+            end = start;                       /* running maximum of the ends */
+        }
+        if (end > M) end = M;
+        for (int64_t k = 0; k < K; ++k) {
+            double amax = 0.0;
+            int finite = 1;
+            for (int64_t r = start; r < end; ++r) {
+                double v = oracle_bf16_value(x[r * K + k]);
+                if (!is_finite_d(v)) finite = 0;
+                else if (fabs(v) > amax) amax = fabs(v);
+            }
+            float mult, stored;
+            if (!finite) {
+                uint32_t nanbits = 0x7FC00000u;
+                memcpy(&mult, &nanbits, sizeof mult);
+                stored = mult;
+            } else {
+                mult = oracle_group_scale_value((float)amax);
+                if (flags & 1) mult = group_pow2_floor(mult);
+                volatile float one = 1.0f;
+                stored = (flags & 2) ? one / mult : mult;
+            }
+            scales[(int64_t)g * K + k] = stored;
+            for (int64_t r = start; r < end; ++r) {
+                uint8_t c = finite ? oracle_group_encode_element(x[r * K + k], mult) : 0x7F;
+                if (layout == 0) q[r * K + k] = c;
+                else q[r + k * M] = c;
+            }
+        }
+        start = end;                           /* the next group starts here */
+    }
+    for (int64_t r = start; r < M; ++r)
+        for (int64_t k = 0; k < K; ++k) {
+            if (layout == 0) q[r * K + k] = 0;
+            else q[r + k * M] = 0;
+        }
+}
+
 /* ------------------------------------------------------------ transpose --- */
 
 /* out (C, R) = transpose of in (R, C), bytes. */

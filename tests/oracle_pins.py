@@ -367,6 +367,72 @@ def check_group_vs_libraries(o, seed=10):
         assert np.array_equal(q, qr), (M, K, sizes)
 
 
+GROUP_POW2, GROUP_INVERSE = 1, 2
+
+
+def _row_multipliers(scales, ends, M):
+    """Per-element multiplier of every row (its group's row of `scales`), NaN for rows in no group."""
+    K = scales.shape[1]
+    out = np.full((M, K), np.nan, np.float32)
+    start = 0
+    for g, e in enumerate(ends):
+        end = min(max(int(e), start), M)
+        out[start:end] = scales[g]
+        start = end
+    return out
+
+
+def check_group_variants(o, seed=17):
+    """Power-of-two and inverse scales against what fixes them: the plain variant is
+    the group scaling pinned above; power-of-two multipliers have a zero significand
+    and lie in (s/2, s]; their codes are the element encoder's (pinned exhaustively)
+    under that multiplier; the column maximum still encodes in [224, 448]; inverse
+    scales are numpy's binary32 1/s and leave the codes unchanged; COL is ROW
+    transposed."""
+    rng = np.random.default_rng(seed)
+    M, K = 257, 40
+    x = _token_matrix(rng, M, K)
+    x[:, 3] = 0                                     # an all-zero column
+    x[7, 5] = 0x7FC0                                # a NaN column in group 0
+    sizes = [100, 0, 57, 1, 99]
+    ends = np.cumsum(sizes).astype(np.int32)
+    q0, s0 = o.group_scale_ex(x, ends, 0, 0)
+    qp, sp = o.group_scale(x, ends, 0)
+    assert np.array_equal(q0, qp) and np.array_equal(s0.view(np.uint32), sp.view(np.uint32))
+    q1, s1 = o.group_scale_ex(x, ends, 0, GROUP_POW2)
+    nan0 = np.isnan(s0)
+    assert np.array_equal(np.isnan(s1), nan0)
+    fin = ~nan0
+    m, _ = np.frexp(s1[fin])
+    assert np.all(m == 0.5), "power-of-two multipliers"
+    assert np.all((s1[fin].astype(np.float64) <= s0[fin]) & (2.0 * s1[fin].astype(np.float64) > s0[fin]))
+    mult = _row_multipliers(s1, ends, M)
+    in_group = ~np.isnan(mult[:, 0])
+    col_nan = np.isnan(mult)
+    ok = in_group[:, None] & ~col_nan
+    enc = o.group_encode_elements(x[ok], mult[ok])
+    assert np.array_equal(q1[ok], enc)
+    assert np.all(q1[in_group[:, None] & col_nan] == 0x7F) and np.all(q1[~in_group] == 0)
+    dec = np.abs(torch.from_numpy(q1.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy())
+    start = 0
+    for g, e in enumerate(ends):
+        end = min(max(int(e), start), M)
+        if end > start:
+            for k in range(K):
+                if fin[g, k] and np.any(x[start:end, k] & 0x7FFF):
+                    assert 224.0 <= dec[start:end, k].max() <= 448.0, (g, k)
+        start = end
+    q2, s2 = o.group_scale_ex(x, ends, 0, GROUP_INVERSE)
+    assert np.array_equal(q2, q0)
+    want = np.float32(1.0) / s0
+    assert np.array_equal(np.isnan(s2), nan0) and np.array_equal(s2[fin].view(np.uint32), want[fin].view(np.uint32))
+    q3, s3 = o.group_scale_ex(x, ends, 0, GROUP_POW2 | GROUP_INVERSE)
+    assert np.array_equal(q3, q1)
+    assert np.array_equal(s3[fin].astype(np.float64) * s1[fin].astype(np.float64), np.ones(fin.sum()))
+    qc, sc = o.group_scale_ex(x, ends, 1, GROUP_POW2 | GROUP_INVERSE)
+    assert np.array_equal(qc, q3.T) and np.array_equal(sc.view(np.uint32), s3.view(np.uint32))
+
+
 def check_group_invariants(o, seed=11):
     rng = np.random.default_rng(seed)
     M, K = 300, 48
@@ -548,6 +614,7 @@ FAST_CHECKS = [
     check_grouped_mm_vs_torch, check_grouped_mm_closed_form, check_grouped_mm_block_scales,
     check_grouped_mm_nan,
     check_mx_rceil_worked_blocks, check_mx_rceil_vs_division, check_mx_axis0_is_transpose,
+    check_group_variants,
 ]
 
 

@@ -47,6 +47,11 @@ MUTATIONS = [
     ("axis0_block_rows", "(a * 32 + i) * K + b;", "(a + i) * K + b;"),
     ("axis0_dequant_scale_row", "s[(m / 32) * K + k]", "s[(m % 32) * K + k]"),
     ("axis1_ex_dequant_scale", "s[m * (K / 32) + k / 32]", "s[m * (K / 32) + k % 32]"),
+    ("group_pow2_rounds_up", "return ldexpf(1.0f, e - 1);", "return ldexpf(1.0f, e);"),
+    ("group_pow2_ignored", "if (flags & 1) mult = group_pow2_floor(mult);", "if (flags & 4) mult = group_pow2_floor(mult);"),
+    ("group_inverse_not_stored", "stored = (flags & 2) ? one / mult : mult;", "stored = mult;"),
+    ("group_codes_from_stored_scale", "oracle_group_encode_element(x[r * K + k], mult)",
+     "oracle_group_encode_element(x[r * K + k], stored)"),
 ]
 
 
