@@ -48,7 +48,7 @@ const char* mxq_status_string(int status)
     case MXQ_ERR_HIP: return "MXQ_ERR_HIP: a HIP runtime call failed";
     case MXQ_ERR_NOT_IMPLEMENTED: return "MXQ_ERR_NOT_IMPLEMENTED";
     case MXQ_ERR_DTYPE: return "MXQ_ERR_DTYPE: unknown output data type";
-    case MXQ_ERR_RULE: return "MXQ_ERR_RULE: unknown scale rule";
+    case MXQ_ERR_RULE: return "MXQ_ERR_RULE: unknown scale rule or flag";
     default: return "unknown mxq_status";
     }
 }
@@ -144,9 +144,18 @@ mxq_status mxq_group_scale_fp8(const void* x_bf16, int64_t M, int64_t K, const i
                                int out_layout, void* q_e4m3, float* scales, void* workspace,
                                size_t workspace_bytes, void* stream)
 {
+    return mxq_group_scale_fp8_ex(x_bf16, M, K, group_end_offs, G, out_layout, 0, q_e4m3, scales, workspace,
+                                  workspace_bytes, stream);
+}
+
+mxq_status mxq_group_scale_fp8_ex(const void* x_bf16, int64_t M, int64_t K, const int32_t* group_end_offs,
+                                  int32_t G, int out_layout, int flags, void* q_e4m3, float* scales,
+                                  void* workspace, size_t workspace_bytes, void* stream)
+{
     mxq_status st = check_group_sizes(M, K, G);
     if (st != MXQ_OK) return st;
     if (out_layout != MXQ_LAYOUT_ROW && out_layout != MXQ_LAYOUT_COL) return MXQ_ERR_LAYOUT;
+    if ((flags & ~(MXQ_GROUP_POW2_SCALE | MXQ_GROUP_INVERSE_SCALE)) != 0) return MXQ_ERR_RULE;
     if (K == 0) return MXQ_OK;
     if (!group_end_offs || !scales) return MXQ_ERR_NULL;
     if (M > 0 && (!x_bf16 || !q_e4m3)) return MXQ_ERR_NULL;
@@ -155,7 +164,7 @@ mxq_status mxq_group_scale_fp8(const void* x_bf16, int64_t M, int64_t K, const i
     const size_t need = mxq::group_scale_workspace_bytes(M, K, G);
     if (!workspace || workspace_bytes < need) return MXQ_ERR_WORKSPACE;
     if (!aligned16(workspace)) return MXQ_ERR_ALIGN;
-    return hip_status(mxq::launch_group_scale(x_bf16, (int)M, (int)K, group_end_offs, (int)G, out_layout,
+    return hip_status(mxq::launch_group_scale(x_bf16, (int)M, (int)K, group_end_offs, (int)G, out_layout, flags,
                                               q_e4m3, scales, workspace, (hipStream_t)stream));
 }
 

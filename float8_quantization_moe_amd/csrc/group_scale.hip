@@ -109,6 +109,9 @@ struct Workspace {
     int32_t* bfirst;      // [ceil(M/128)] group containing the first row of each 128-row block (G: none)
     uint32_t* deferred;   // [slots][S] 1 if the tile was left for the deferred kernel
     uint32_t* any;        // [1] 1 if any tile needs the deferred kernel
+    float* inv_out;       // the caller's (G, K) scales when they hold 1/s (the kernels then keep the
+                          // multipliers s in a workspace array); NULL when they hold s itself
+    int pow2;             // 1: multipliers rounded down to a power of two
 };
 
 static size_t align256(size_t n) { return (n + 255) / 256 * 256; }
@@ -116,7 +119,7 @@ static size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 static int64_t chunk_slots(int64_t M, int R, int64_t G) { return (M + R - 1) / R + G + 1; }
 
 template <int LAYOUT>
-static size_t workspace_layout(int64_t M, int64_t K, int64_t G, size_t off[9])
+static size_t workspace_layout(int64_t M, int64_t K, int64_t G, size_t off[10])
 {
     using C = TileCfg<LAYOUT>;
     const int64_t slots = chunk_slots(M, C::R, G);
@@ -131,6 +134,7 @@ static size_t workspace_layout(int64_t M, int64_t K, int64_t G, size_t off[9])
     off[6] = o; o += align256((size_t)(G * 4));
     off[7] = o; o += align256((size_t)(((M + 127) / 128 + 1) * 4));
     off[8] = o; o += align256((size_t)(G * 8));
+    off[9] = o; o += align256((size_t)(G * K * 4));       // multipliers when the caller asked for 1/s
     return o;
 }
 
@@ -148,18 +152,29 @@ bool group_scale_sizes_ok(int64_t M, int64_t K, int64_t G)
 
 size_t group_scale_workspace_bytes(int64_t M, int64_t K, int32_t G)
 {
-    size_t off[9];
+    size_t off[10];
     const size_t a = workspace_layout<0>(M, K, G, off);
     const size_t b = workspace_layout<1>(M, K, G, off);
     return a > b ? a : b;
 }
 
 // ------------------------------------------------------------- helpers ----
-__device__ __forceinline__ float group_scale_of(uint32_t amax_bits)
+// The multiplier of a column: 448 / max(amax, 1e-12) (correctly rounded divide),
+// or that rounded down to a power of two (clearing the significand: the
+// quotient is always a positive normal, between 448 / bf16 max and 448 / 1e-12).
+__device__ __forceinline__ float group_scale_of(uint32_t amax_bits, int pow2)
 {
     if (amax_bits >= 0x7F80u) return __uint_as_float(0x7FC00000u);   // Inf/NaN in the column
     const float amax = __uint_as_float(amax_bits << 16);
-    return 448.0f / fmaxf(amax, 1e-12f);                            // correctly rounded divide
+    const float s = 448.0f / fmaxf(amax, 1e-12f);
+    return pow2 ? __uint_as_float(__float_as_uint(s) & 0xFF800000u) : s;
+}
+
+// The stored inverse 1/s of a multiplier (one correctly rounded divide; NaN kept).
+__device__ __forceinline__ float4 inverse4(float4 m)
+{
+    const auto inv = [](float v) { return v != v ? v : 1.0f / v; };
+    return make_float4(inv(m.x), inv(m.y), inv(m.z), inv(m.w));
 }
 
 struct ColScales {
@@ -480,7 +495,8 @@ void group_plan_kernel(const int32_t* __restrict__ offs, int G, int M, int K, Wo
     __shared__ int sh_st[kWave], sh_en[kWave], sh_first[kWave], sh_cnt[kWave];
     __shared__ int sh_base_chunk, sh_end_chunk;
     __shared__ unsigned long long sh_empty;
-    const float s_empty = group_scale_of(0u);
+    const float s_empty = group_scale_of(0u, ws.pow2);
+    const float s_empty_out = ws.inv_out ? 1.0f / s_empty : s_empty;
     int carry_end = 0, carry_cnt = 0;      // meaningful in wave 0 only
     for (int base = 0; base < G + 1; base += kWave) {   // groups 0..G-1, then the rows past the last end
         if (threadIdx.x < kWave) {
@@ -542,8 +558,9 @@ void group_plan_kernel(const int32_t* __restrict__ offs, int G, int M, int K, Wo
         if (M == 0) {
             for (unsigned long long mm = sh_empty; mm; mm &= mm - 1) {
                 const int g = base + __builtin_ctzll(mm);
+                float* out = ws.inv_out ? ws.inv_out : scales;
                 for (int k = (int)threadIdx.x * 4; k < K; k += kGThreads * 4)
-                    *(float4*)(scales + (int64_t)g * K + k) = make_float4(s_empty, s_empty, s_empty, s_empty);
+                    *(float4*)(out + (int64_t)g * K + k) = make_float4(s_empty_out, s_empty_out, s_empty_out, s_empty_out);
             }
         }
         __syncthreads();
@@ -557,15 +574,15 @@ void group_plan_kernel(const int32_t* __restrict__ offs, int G, int M, int K, Wo
     }
 }
 
-__device__ __forceinline__ float4 scales_lo(uint4 a)
+__device__ __forceinline__ float4 scales_lo(uint4 a, int pow2)
 {
-    return make_float4(group_scale_of(a.x & 0xFFFFu), group_scale_of(a.x >> 16),
-                       group_scale_of(a.y & 0xFFFFu), group_scale_of(a.y >> 16));
+    return make_float4(group_scale_of(a.x & 0xFFFFu, pow2), group_scale_of(a.x >> 16, pow2),
+                       group_scale_of(a.y & 0xFFFFu, pow2), group_scale_of(a.y >> 16, pow2));
 }
-__device__ __forceinline__ float4 scales_hi(uint4 a)
+__device__ __forceinline__ float4 scales_hi(uint4 a, int pow2)
 {
-    return make_float4(group_scale_of(a.z & 0xFFFFu), group_scale_of(a.z >> 16),
-                       group_scale_of(a.w & 0xFFFFu), group_scale_of(a.w >> 16));
+    return make_float4(group_scale_of(a.z & 0xFFFFu, pow2), group_scale_of(a.z >> 16, pow2),
+                       group_scale_of(a.w & 0xFFFFu, pow2), group_scale_of(a.w >> 16, pow2));
 }
 __device__ __forceinline__ uint4 f4_bits(float4 f)
 {
@@ -626,9 +643,12 @@ __device__ __forceinline__ void write_empty_group_scales(int G, int K, const Wor
                                                          int nthreads)
 {
     if ((int)blockIdx.x < G && ws.empty[blockIdx.x] != 0u) {
-        const float s_empty = group_scale_of(0u);
-        for (int kk = (int)threadIdx.x * 4; kk < K; kk += nthreads * 4)
-            *(float4*)(scales + (int64_t)blockIdx.x * K + kk) = make_float4(s_empty, s_empty, s_empty, s_empty);
+        const float s_empty = group_scale_of(0u, ws.pow2);
+        const float4 e4 = make_float4(s_empty, s_empty, s_empty, s_empty);
+        for (int kk = (int)threadIdx.x * 4; kk < K; kk += nthreads * 4) {
+            *(float4*)(scales + (int64_t)blockIdx.x * K + kk) = e4;
+            if (ws.inv_out) *(float4*)(ws.inv_out + (int64_t)blockIdx.x * K + kk) = inverse4(e4);
+        }
     }
 }
 
@@ -733,7 +753,7 @@ __device__ __forceinline__ void reduce_strip(const uint16_t* __restrict__ x, con
     __syncthreads();
     if (rs == 0) {
         max_rows(a, &sh.red[0][cg], C::NS, C::CG);
-        const float4 lo = scales_lo(a), hi = scales_hi(a);
+        const float4 lo = scales_lo(a, ws.pow2), hi = scales_hi(a, ws.pow2);
         *(float4*)(sh.scale + cg * 8) = lo;
         *(float4*)(sh.scale + cg * 8 + 4) = hi;
         if (k < K) {
@@ -744,6 +764,10 @@ __device__ __forceinline__ void reduce_strip(const uint16_t* __restrict__ x, con
             } else {
                 *(float4*)dst = lo;
                 *(float4*)(dst + 4) = hi;
+            }
+            if (ws.inv_out) {                              // the caller's 1/s (read by no kernel)
+                *(float4*)(ws.inv_out + (int64_t)t.g * K + k) = inverse4(lo);
+                *(float4*)(ws.inv_out + (int64_t)t.g * K + k + 4) = inverse4(hi);
             }
         }
     }
@@ -832,8 +856,8 @@ void group_hold_kernel(const uint16_t* __restrict__ x, int M, int K, int G, int 
             __syncthreads();
             if (rs == 0) {
                 max_rows(a, &sh.red[0][cg], C::NS, C::CG);
-                *(float4*)(sh.scale + cg * 8) = scales_lo(a);
-                *(float4*)(sh.scale + cg * 8 + 4) = scales_hi(a);
+                *(float4*)(sh.scale + cg * 8) = scales_lo(a, ws.pow2);
+                *(float4*)(sh.scale + cg * 8 + 4) = scales_hi(a, ws.pow2);
             }
             __syncthreads();
         }
@@ -905,8 +929,13 @@ void group_finalize_kernel(int K, int SF, Workspace ws, float* __restrict__ scal
     if (rs == 0 && k < K) {
 #pragma unroll
         for (int r = 1; r < kFNS; ++r) max8(a, red[r][cg]);
-        *(float4*)(scales + (int64_t)g * K + k) = scales_lo(a);
-        *(float4*)(scales + (int64_t)g * K + k + 4) = scales_hi(a);
+        const float4 lo = scales_lo(a, ws.pow2), hi = scales_hi(a, ws.pow2);
+        *(float4*)(scales + (int64_t)g * K + k) = lo;
+        *(float4*)(scales + (int64_t)g * K + k + 4) = hi;
+        if (ws.inv_out) {
+            *(float4*)(ws.inv_out + (int64_t)g * K + k) = inverse4(lo);
+            *(float4*)(ws.inv_out + (int64_t)g * K + k + 4) = inverse4(hi);
+        }
     }
 }
 
@@ -1068,11 +1097,11 @@ void group_deferred_kernel(const uint16_t* __restrict__ x, int M, int K, int G, 
 
 // --------------------------------------------------------------- launch ---
 template <int LAYOUT>
-static hipError_t launch_layout(const void* x, int M, int K, const int32_t* offs, int G, void* q, float* scales,
-                                void* workspace, hipStream_t stream)
+static hipError_t launch_layout(const void* x, int M, int K, const int32_t* offs, int G, int flags, void* q,
+                                float* out_scales, void* workspace, hipStream_t stream)
 {
     using C = TileCfg<LAYOUT>;
-    size_t off[9];
+    size_t off[10];
     workspace_layout<LAYOUT>(M, K, G, off);
     uint8_t* base = (uint8_t*)workspace;
     Workspace ws;
@@ -1085,6 +1114,13 @@ static hipError_t launch_layout(const void* x, int M, int K, const int32_t* offs
     ws.gend = (int32_t*)(base + off[6]);
     ws.bfirst = (int32_t*)(base + off[7]);
     ws.gchunks = (int32_t*)(base + off[8]);
+    // Every kernel reads and writes the multipliers s through `scales`: the
+    // caller's array, or a workspace array when the caller asked for 1/s, which
+    // the writers of s then also store in the caller's array.
+    const bool inverse = (flags & 2) != 0;
+    float* scales = inverse ? (float*)(base + off[9]) : out_scales;
+    ws.inv_out = inverse ? out_scales : nullptr;
+    ws.pow2 = (flags & 1) ? 1 : 0;
     const int S = (K + C::W - 1) / C::W;
     const int64_t slots = chunk_slots(M, C::R, G);
     const int nGS = G * S;
@@ -1162,11 +1198,11 @@ static hipError_t launch_layout(const void* x, int M, int K, const int32_t* offs
     return hipGetLastError();
 }
 
-hipError_t launch_group_scale(const void* x, int M, int K, const int32_t* offs, int G, int layout,
+hipError_t launch_group_scale(const void* x, int M, int K, const int32_t* offs, int G, int layout, int flags,
                               void* q, float* scales, void* workspace, hipStream_t stream)
 {
-    return layout == 0 ? launch_layout<0>(x, M, K, offs, G, q, scales, workspace, stream)
-                       : launch_layout<1>(x, M, K, offs, G, q, scales, workspace, stream);
+    return layout == 0 ? launch_layout<0>(x, M, K, offs, G, flags, q, scales, workspace, stream)
+                       : launch_layout<1>(x, M, K, offs, G, flags, q, scales, workspace, stream);
 }
 
 }  // namespace mxq

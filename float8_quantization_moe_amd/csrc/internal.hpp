@@ -17,7 +17,7 @@ hipError_t launch_mx_dequantize(const void* q, const void* s, int64_t M, int64_t
 
 bool group_scale_sizes_ok(int64_t M, int64_t K, int64_t G);
 size_t group_scale_workspace_bytes(int64_t M, int64_t K, int32_t G);
-hipError_t launch_group_scale(const void* x, int M, int K, const int32_t* offs, int G, int layout,
+hipError_t launch_group_scale(const void* x, int M, int K, const int32_t* offs, int G, int layout, int flags,
                               void* q, float* scales, void* workspace, hipStream_t stream);
 
 int grouped_mm_max_groups();

@@ -32,11 +32,13 @@ MXQ_OUT_BF16 = 0
 MXQ_OUT_F32 = 1
 MXQ_SCALE_FLOOR = 0
 MXQ_SCALE_RCEIL = 1
+MXQ_GROUP_POW2_SCALE = 1
+MXQ_GROUP_INVERSE_SCALE = 2
 
 EXPORTED = ("mxq_abi_version", "mxq_status_string", "mxq_last_hip_error", "mxq_quantize_mx",
             "mxq_dequantize_mx", "mxq_group_scale_workspace_bytes", "mxq_group_scale_fp8",
             "mxq_transpose_u8", "mxq_grouped_mm_workspace_bytes", "mxq_scaled_grouped_mm",
-            "mxq_quantize_mx_ex", "mxq_dequantize_mx_ex")
+            "mxq_quantize_mx_ex", "mxq_dequantize_mx_ex", "mxq_group_scale_fp8_ex")
 
 
 class MxqError(RuntimeError):
@@ -78,6 +80,8 @@ def lib() -> ctypes.CDLL:
         L.mxq_group_scale_workspace_bytes.argtypes = [i64, i64, i32]
         L.mxq_group_scale_fp8.restype = ctypes.c_int
         L.mxq_group_scale_fp8.argtypes = [P, i64, i64, P, i32, ctypes.c_int, P, P, P, sz, P]
+        L.mxq_group_scale_fp8_ex.restype = ctypes.c_int
+        L.mxq_group_scale_fp8_ex.argtypes = [P, i64, i64, P, i32, ctypes.c_int, ctypes.c_int, P, P, P, sz, P]
         L.mxq_transpose_u8.restype = ctypes.c_int
         L.mxq_transpose_u8.argtypes = [P, i64, i64, P, P]
         L.mxq_grouped_mm_workspace_bytes.restype = sz
@@ -194,6 +198,24 @@ def mxq_group_scale_fp8(x: torch.Tensor, group_end_offs: torch.Tensor, out_layou
     wbytes = workspace.numel() * workspace.element_size()
     _check(lib().mxq_group_scale_fp8(px, M, K, po, G, int(out_layout), pq, ps, pw, wbytes, _stream(stream)),
            "mxq_group_scale_fp8")
+
+
+def mxq_group_scale_fp8_ex(x: torch.Tensor, group_end_offs: torch.Tensor, out_layout: int, flags: int,
+                           q: torch.Tensor, scales: torch.Tensor, workspace: torch.Tensor,
+                           stream=None) -> None:
+    """mxq_group_scale_fp8 with flags MXQ_GROUP_POW2_SCALE / MXQ_GROUP_INVERSE_SCALE."""
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D (M, K)")
+    M, K = x.shape
+    G = group_end_offs.numel()
+    px = _dev(x, "x", torch.bfloat16)
+    po = _dev(group_end_offs, "group_end_offs", torch.int32)
+    pq = _dev(q, "q", torch.uint8, M * K)
+    ps = _dev(scales, "scales", torch.float32, G * K)
+    pw = _dev(workspace, "workspace")
+    wbytes = workspace.numel() * workspace.element_size()
+    _check(lib().mxq_group_scale_fp8_ex(px, M, K, po, G, int(out_layout), int(flags), pq, ps, pw, wbytes,
+                                        _stream(stream)), "mxq_group_scale_fp8_ex")
 
 
 def mxq_transpose_u8(inp: torch.Tensor, out: torch.Tensor, stream=None) -> None:

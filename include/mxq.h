@@ -60,7 +60,7 @@ typedef enum mxq_status {
     MXQ_ERR_HIP = 6,         /* a HIP runtime call failed (launch, device query)    */
     MXQ_ERR_NOT_IMPLEMENTED = 7,
     MXQ_ERR_DTYPE = 8,       /* unknown mxq_out_dtype value                         */
-    MXQ_ERR_RULE = 9         /* unknown mxq_scale_rule value                        */
+    MXQ_ERR_RULE = 9         /* unknown mxq_scale_rule value or group flag          */
 } mxq_status;
 
 typedef enum mxq_layout {
@@ -76,6 +76,11 @@ typedef enum mxq_scale_rule {
     MXQ_SCALE_RCEIL = 1      /* round the scale up: the smallest e with
                                 amax <= 448 * 2^e, so nothing saturates             */
 } mxq_scale_rule;
+
+typedef enum mxq_group_flags {
+    MXQ_GROUP_POW2_SCALE = 1,    /* multipliers rounded down to a power of two      */
+    MXQ_GROUP_INVERSE_SCALE = 2  /* store 1/s (dequantization factor) instead of s  */
+} mxq_group_flags;
 
 typedef enum mxq_out_dtype {
     MXQ_OUT_BF16 = 0,        /* bfloat16, rounded to nearest even from the fp32 sum  */
@@ -207,6 +212,28 @@ mxq_status mxq_group_scale_fp8(const void* x_bf16, int64_t M, int64_t K,
                                const int32_t* group_end_offs, int32_t G, int out_layout,
                                void* q_e4m3, float* scales,
                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Group-scaling variants: mxq_group_scale_fp8 with `flags`, a bitwise OR of
+ *   MXQ_GROUP_POW2_SCALE     the multiplier is rounded down to a power of two,
+ *                            s' = 2^floor(log2 s) (so amax * s' <= 448 still and
+ *                            x * s' is exact); the codes use s';
+ *   MXQ_GROUP_INVERSE_SCALE  `scales` receives the dequantization factor 1/s
+ *                            (one correctly rounded binary32 division; NaN stays
+ *                            NaN) instead of the multiplier; the codes do not
+ *                            change.
+ * flags == 0 is exactly mxq_group_scale_fp8.  Any other bit: MXQ_ERR_RULE.
+ * Source: "[moe training] fix uncoalesced global accesses in per group rowwise
+ * scaling kernel", Summary (the per-group scaling of the grouped GEMM's
+ * operands); the pages fix neither the rounding of the scale nor which of s and
+ * 1/s is stored, so both are offered.  Arguments, sizes, errors, workspace
+ * (the same mxq_group_scale_workspace_bytes) and clamping as for
+ * mxq_group_scale_fp8.
+ */
+mxq_status mxq_group_scale_fp8_ex(const void* x_bf16, int64_t M, int64_t K,
+                                  const int32_t* group_end_offs, int32_t G, int out_layout, int flags,
+                                  void* q_e4m3, float* scales,
+                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Byte transpose: out (C, R) = in (R, C)^T, both row-major.  The layout

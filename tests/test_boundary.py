@@ -30,7 +30,7 @@ def test_header_declares_the_entry_points():
     for n in ("mxq_quantize_mx", "mxq_dequantize_mx", "mxq_group_scale_fp8",
               "mxq_group_scale_workspace_bytes", "mxq_transpose_u8", "mxq_abi_version",
               "mxq_grouped_mm_workspace_bytes", "mxq_scaled_grouped_mm", "mxq_quantize_mx_ex",
-              "mxq_dequantize_mx_ex"):
+              "mxq_dequantize_mx_ex", "mxq_group_scale_fp8_ex"):
         assert n in names
 
 
@@ -124,6 +124,13 @@ def test_group_scale_argument_errors(L):
     assert f(A, 512, 256, A + 2, 4, 0, A, A, A, ws, S) == 3       # misaligned offsets
     assert f(A, 512, 256, A, 4, 0, A, A + 4, A, ws, S) == 3       # misaligned scales
     assert f(A, 512, 0, A, 4, 0, A, A, A, ws, S) == 0             # K == 0: no-op
+    fx = L.mxq_group_scale_fp8_ex
+    assert fx(A, 512, 256, A, 4, 0, 4, A, A, A, ws, S) == 9      # unknown flag bit
+    assert fx(A, 512, 256, A, 4, 0, -1, A, A, A, ws, S) == 9
+    assert fx(A, 512, 256, A, 4, 2, 1, A, A, A, ws, S) == 4      # layout before flags
+    assert fx(A, 512, 252, A, 4, 0, 3, A, A, A, ws, S) == 2
+    assert fx(A, 512, 256, A, 4, 0, 3, A, A, A, ws - 1, S) == 5
+    assert fx(A, 512, 0, A, 4, 0, 3, A, A, A, ws, S) == 0
 
 
 def test_transpose_argument_errors(L):

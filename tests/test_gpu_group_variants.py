@@ -1,0 +1,168 @@
+"""Group-scaling variants on the GPU -- power-of-two multipliers, inverse stored
+scales, and the other operand of the weight-gradient GEMM -- bit-exact against
+the CPU oracle (codes byte for byte, scales bit for bit).
+
+"[moe training] fix uncoalesced global accesses in per group rowwise scaling
+kernel", Summary: per-group scaling of the grouped GEMM's operands; the pages
+fix neither the rounding of the scale nor whether s or 1/s is stored (readings
+of this repository), and the same kernel scales either operand of the
+weight-gradient product.
+"""
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import pytest
+import torch
+
+import gpu_util as U
+import oracle
+import workloads as W
+from float8_quantization_moe_amd import mxq
+
+pytestmark = pytest.mark.gpu
+
+ROW, COL = mxq.MXQ_LAYOUT_ROW, mxq.MXQ_LAYOUT_COL
+POW2, INV = mxq.MXQ_GROUP_POW2_SCALE, mxq.MXQ_GROUP_INVERSE_SCALE
+FLAGS = [POW2, INV, POW2 | INV]
+FIDS = ["pow2", "inverse", "pow2+inverse"]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "these tests need an MI355X"
+    mxq.lib()
+    yield
+
+
+def oracle_group_ex(x_bits, ends, flags):
+    """Row-layout codes and (G, K) scales of the oracle's variant, columns split across threads."""
+    M, K = x_bits.shape
+    q = np.empty((M, K), np.uint8)
+    scales = np.empty((len(ends), K), np.float32)
+    step = max(8, -(-K // (U.THREADS * 2)))
+    cols = [(a, min(K, a + step)) for a in range(0, K, step)]
+
+    def run(sl):
+        a, b = sl
+        qq, ss = oracle.group_scale_ex(np.ascontiguousarray(x_bits[:, a:b]), ends, oracle.LAYOUT_ROW, flags)
+        q[:, a:b] = qq
+        scales[:, a:b] = ss
+
+    with ThreadPoolExecutor(U.THREADS) as ex:
+        list(ex.map(run, cols))
+    return q, scales.view(np.uint32)
+
+
+def run_group_ex(x, ends, layout, flags, M, K):
+    G = len(ends)
+    offs = torch.tensor(np.asarray(ends, np.int32), device="cuda")
+    qg = U.Guarded(M * K, torch.uint8, (M, K) if layout == ROW else (K, M))
+    sg = U.Guarded(G * K, torch.float32, (G, K))
+    ws = torch.empty(max(16, mxq.mxq_group_scale_workspace_bytes(M, K, G)), dtype=torch.uint8, device="cuda")
+    ws.fill_(0xAB)
+    mxq.mxq_group_scale_fp8_ex(x, offs, layout, flags, qg.t, sg.t, ws)
+    torch.cuda.synchronize()
+    assert qg.guard_intact() and sg.guard_intact(), "wrote past the end"
+    return U.host_u8(qg.t), U.host_f32_bits(sg.t)
+
+
+def check_variant(x_bits, ends, flags, layouts=(ROW, COL), name=""):
+    M, K = x_bits.shape
+    print(f"case {name} M={M} K={K} G={len(ends)} flags={flags}", flush=True)
+    want_q, want_s = oracle_group_ex(x_bits, ends, flags)
+    x = U.dev_bf16(x_bits)
+    for layout in layouts:
+        q, s = run_group_ex(x, ends, layout, flags, M, K)
+        assert np.array_equal(s, want_s), f"{name} layout {layout} scales: {U.first_mismatch(s, want_s)}"
+        qr = q if layout == ROW else q.T
+        assert np.array_equal(qr, want_q), f"{name} layout {layout} codes: {U.first_mismatch(qr, want_q)}"
+
+
+def _bits(rng, M, K):
+    x = (rng.standard_normal((M, K)) * np.exp(rng.standard_normal((M, 1)))).astype(np.float32)
+    return (x.view(np.uint32) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("flags", FLAGS, ids=FIDS)
+def test_tiny(flags):
+    check_variant(W.bf16_bits(W.tiny_x(0)), W.tiny_group_ends(), flags, name="tiny")
+
+
+EDGE = {
+    "empty_groups": (400, 72, [0, 150, 0, 0, 250, 0]),
+    "one_row_groups": (130, 40, [1] * 70 + [60]),
+    "tail_rows": (1000, 520, [129, 127, 1, 255, 300]),
+}
+
+
+@pytest.mark.parametrize("mode", ["hold", "twopass"])
+@pytest.mark.parametrize("flags", FLAGS, ids=FIDS)
+@pytest.mark.parametrize("case", list(EDGE), ids=list(EDGE))
+def test_edge_cases(case, flags, mode, monkeypatch):
+    monkeypatch.setenv("MXQ_GROUP_MODE", mode)
+    M, K, sizes = EDGE[case]
+    rng = np.random.default_rng(M + K)
+    x_bits = _bits(rng, M, K)
+    x_bits[:, 5] = 0                        # an all-zero column
+    x_bits[3, 9] = 0x7F80                   # a non-finite column
+    check_variant(x_bits, np.cumsum(sizes).astype(np.int32), flags, name=case)
+
+
+ROUTES = {
+    "held": {"MXQ_GROUP_MODE": "hold"},
+    "all_streamed": {"MXQ_GROUP_MODE": "hold", "MXQ_GROUP_HOLD_TILES": "0"},
+    "time_outs_deferred": {"MXQ_GROUP_MODE": "hold", "MXQ_GROUP_HOLD_TILES": "5", "MXQ_GROUP_WAIT_US": "0"},
+    "all_waits_time_out": {"MXQ_GROUP_MODE": "hold", "MXQ_GROUP_WAIT_US": "0"},
+}
+
+
+@pytest.mark.parametrize("route", list(ROUTES), ids=list(ROUTES))
+def test_routes_pow2_inverse(route, monkeypatch):
+    """Every route of the hold method writes the multipliers it uses and the stored 1/s."""
+    for k, v in ROUTES[route].items():
+        monkeypatch.setenv(k, v)
+    rng = np.random.default_rng(41)
+    x_bits = _bits(rng, 3000, 1040)
+    check_variant(x_bits, np.cumsum([1500, 0, 700, 3, 597, 200]).astype(np.int32), POW2 | INV, name=route)
+
+
+@pytest.mark.parametrize("flags", FLAGS, ids=FIDS)
+def test_zero_rows_writes_scales_only(flags):
+    K, G = 64, 3
+    x = torch.empty((0, K), dtype=torch.bfloat16, device="cuda")
+    want_q, want_s = oracle_group_ex(np.zeros((0, K), np.uint16), np.zeros(G, np.int32), flags)
+    q, s = run_group_ex(x, np.zeros(G, np.int32), ROW, flags, 0, K)
+    assert np.array_equal(s, want_s)
+
+
+@pytest.fixture(scope="module")
+def tokens_bits():
+    return W.bf16_bits(W.moe_tokens())
+
+
+@pytest.mark.parametrize("flags", [POW2, POW2 | INV], ids=["pow2", "pow2+inverse"])
+def test_tokens_full_size(tokens_bits, flags):
+    """(16640, 5120): 16 Zipf groups row-major and 128 column-major, as in the benchmark."""
+    M, K = tokens_bits.shape
+    x = U.dev_bf16(tokens_bits)
+    for G, layout in ((16, ROW), (128, COL)):
+        ends = W.zipf_group_ends(M, G)
+        print(f"tokens G={G} layout={layout} flags={flags}", flush=True)
+        want_q, want_s = oracle_group_ex(tokens_bits, ends, flags)
+        q, s = run_group_ex(x, ends, layout, flags, M, K)
+        assert np.array_equal(s, want_s), U.first_mismatch(s, want_s)
+        qr = q if layout == ROW else q.T
+        assert np.array_equal(qr, want_q), U.first_mismatch(qr, want_q)
+
+
+@pytest.mark.parametrize("flags", [0, POW2], ids=["plain", "pow2"])
+def test_wgrad_other_operand(flags):
+    """The other operand of the weight-gradient product dW_g = dY_g^T X_g: the
+    output gradient dY (16640 tokens, 8192 expert features) grouped by the same
+    16 Zipf groups, column-major (token-contiguous) as the GEMM contracts over
+    tokens.  The same kernel, at its own shape."""
+    M, N = 16640, 8192
+    rng = np.random.default_rng(5)
+    dy = _bits(rng, M, N)
+    ends = W.zipf_group_ends(M, 16)
+    check_variant(dy, ends, flags, layouts=(COL,), name="dY (16640, 8192)")
