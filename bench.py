@@ -47,6 +47,7 @@ HBM_PEAK_GBPS = 8000.0                     # MI355X HBM3E, 8 TB/s
 DISPATCH = (65536, 5120)
 TOKENS = (16640, 5120)
 G_ROW, G_COL = 16, 128
+WGRAD_N = 8192                     # expert feature width of the output gradient dY (the wgrad operand)
 EXPERTS = (16, 8192, 5120)                 # (G, N, K) of the grouped GEMM
 MFMA_FP8_PEAK_TFLOPS = 5000.0              # MI355X dense fp8 matrix peak
 PROFILES = os.path.join(HERE, "profiles")
@@ -370,12 +371,17 @@ def main():
     # Variants of the path's calls (the NEXT rows), each alone on the same rotated
     # buffers and shapes; reported beside the step, not part of `value`.
     FLOOR, RCEIL = mxq.MXQ_SCALE_FLOOR, mxq.MXQ_SCALE_RCEIL
+    POW2, INV = mxq.MXQ_GROUP_POW2_SCALE, mxq.MXQ_GROUP_INVERSE_SCALE
     s_dim0 = lambda b: b.s1.view(M1 // 32, K1)      # (M/32, K) scales: the same byte count as (M, K/32)
     variant_calls = [
         ("mx_quantize_rows_rceil", mx_bytes(M1, K1), lambda b: mxq.mxq_quantize_mx_ex(b.x1, 1, RCEIL, b.q1, b.s1, stream)),
         ("mx_quantize_cols_floor", mx_bytes(M1, K1), lambda b: mxq.mxq_quantize_mx_ex(b.x1, 0, FLOOR, b.q1, s_dim0(b), stream)),
         ("mx_quantize_cols_rceil", mx_bytes(M1, K1), lambda b: mxq.mxq_quantize_mx_ex(b.x1, 0, RCEIL, b.q1, s_dim0(b), stream)),
         ("mx_dequantize_cols", mx_bytes(M1, K1), lambda b: mxq.mxq_dequantize_mx_ex(b.q1, s_dim0(b), 0, b.y1, stream)),
+        ("group_scale_g16_row_pow2_inverse", group_bytes(M2, K2, G_ROW),
+         lambda b: mxq.mxq_group_scale_fp8_ex(b.x2, offs16, ROW, POW2 | INV, b.q2, b.sc2, ws, stream)),
+        ("group_scale_g128_col_pow2_inverse", group_bytes(M2, K2, G_COL),
+         lambda b: mxq.mxq_group_scale_fp8_ex(b.x3, offs128, COL, POW2 | INV, b.q3, b.sc3, ws, stream)),
     ]
     variants = {}
     for name, nbytes, fn in variant_calls:
@@ -391,7 +397,29 @@ def main():
         us = e0.elapsed_time(e1) * 1e3 / reps
         variants[name] = {"avg_us": round(us, 2), "algorithmic_bytes": nbytes, "GBps": round(nbytes / (us * 1e3), 1),
                           "frac_of_peak": round(nbytes / (us * 1e3) / HBM_PEAK_GBPS, 4),
-                          "shape": [M1, K1]}
+                          "shape": [M1, K1] if name.startswith("mx_") else [M2, K2]}
+    # the other operand of the weight-gradient GEMM: dY (16640, 8192), 16 groups, column-major
+    dy = [torch.empty((M2, WGRAD_N), dtype=torch.bfloat16, device=dev).normal_() for _ in range(min(2, len(sets)))]
+    qdy = torch.empty((WGRAD_N, M2), dtype=torch.uint8, device=dev)
+    sdy = torch.empty((G_ROW, WGRAD_N), dtype=torch.float32, device=dev)
+    wsdy = torch.empty(mxq.mxq_group_scale_workspace_bytes(M2, WGRAD_N, G_ROW), dtype=torch.uint8, device=dev)
+    fn = lambda i: mxq.mxq_group_scale_fp8(dy[i % len(dy)], offs16, COL, qdy, sdy, wsdy, stream)
+    for i in range(2):
+        fn(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for r in range(reps):
+        fn(r)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    nb = group_bytes(M2, WGRAD_N, G_ROW)
+    variants["group_scale_wgrad_dy_g16_col"] = {"avg_us": round(us, 2), "algorithmic_bytes": nb,
+                                                "GBps": round(nb / (us * 1e3), 1),
+                                                "frac_of_peak": round(nb / (us * 1e3) / HBM_PEAK_GBPS, 4),
+                                                "shape": [M2, WGRAD_N]}
+    del dy, qdy, sdy, wsdy
     for i in range(2):
         step(i)
     torch.cuda.synchronize()
