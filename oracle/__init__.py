@@ -68,6 +68,7 @@ _SIGS = {
     "oracle_group_scale": (None, [_P, _i64, _i64, _P, _i32, ctypes.c_int, _P, _P]),
     "oracle_group_scale_ex": (None, [_P, _i64, _i64, _P, _i32, ctypes.c_int, ctypes.c_int, _P, _P]),
     "oracle_transpose_u8": (None, [_P, _i64, _i64, _P]),
+    "oracle_dispatch_pack": (None, [_P, _i64, _i64, _P, _i32, _i32, _P, _P, _P]),
     "oracle_mx_encode_elements": (None, [_P, _P, _i64, _P]),
     "oracle_mx_decode_elements": (None, [_P, _P, _i64, _P]),
     "oracle_e4m3_encode_f32_array": (None, [_P, _i64, _P]),
@@ -214,6 +215,25 @@ class Oracle:
         scales = np.empty((G, K), np.float32)
         self._L.oracle_group_scale_ex(_ptr(x), M, K, _ptr(ends), G, int(layout), int(flags), _ptr(q), _ptr(scales))
         return q, scales
+
+    def dispatch_pack(self, x_bits, expert_ids, E: int):
+        """Dispatch pack: x (M, K) bf16 bits, expert_ids (M, topk) int32 -> (packed
+        (M*topk, K + K/32) uint8 rows [e4m3 codes | e8m0 scales] ordered stably by
+        expert, src_pair (M*topk,) int32 pair index t*topk + j of each row (-1 past
+        the last end), group_end (E,) int32).  Rows past the last end are zero here
+        (the oracle writes nothing there)."""
+        x = _as_u16(x_bits)
+        M, K = x.shape
+        ids = np.ascontiguousarray(np.asarray(expert_ids, dtype=np.int32))
+        if ids.ndim != 2 or ids.shape[0] != M or K % 32 or E < 1:
+            raise ValueError("expert_ids must be (M, topk), K a multiple of 32, E >= 1")
+        topk = ids.shape[1]
+        P = M * topk
+        packed = np.zeros((P, K + K // 32), np.uint8)
+        src = np.empty(P, np.int32)
+        ends = np.empty(E, np.int32)
+        self._L.oracle_dispatch_pack(_ptr(x), M, K, _ptr(ids), topk, E, _ptr(packed), _ptr(src), _ptr(ends))
+        return packed, src, ends
 
     def transpose_u8(self, a):
         a = np.ascontiguousarray(a, dtype=np.uint8)

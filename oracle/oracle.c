@@ -428,6 +428,36 @@ void oracle_group_scale_ex(const uint16_t* x, int64_t M, int64_t K,
         }
 }
 
+/* ------------------------------------------------------- dispatch pack --- */
+/* [A2A] Summary: the payload of the expert-parallel all-to-all is quantized to
+ * MXFP8 and sent as e4m3 data plus e8m0 scales.  The dispatch pack builds that
+ * payload in one step (a reading of this repository, the pages show the two
+ * buffers only): token t with expert ids[t*topk + j] (j < topk) contributes one
+ * row per (t, j) pair, the pairs are ordered by expert, stably (by pair index
+ * p = t*topk + j within an expert), and each row is the token's MX encoding
+ * packed as [K e4m3 codes | K/32 e8m0 scales] (row stride K + K/32 bytes), so
+ * that one buffer carries both parts of every row.  Pairs whose expert id is
+ * outside [0, E) are dropped.  src_pair[r] is the pair index of row r;
+ * group_end[e] is the number of kept pairs with expert <= e.  Rows at or past
+ * group_end[E-1] are not written (their src_pair is -1). */
+void oracle_dispatch_pack(const uint16_t* x, int64_t M, int64_t K, const int32_t* ids, int32_t topk,
+                          int32_t E, uint8_t* packed, int32_t* src_pair, int32_t* group_end)
+{
+    const int64_t P = M * topk, ldp = K + K / 32;
+    int64_t r = 0;
+    for (int32_t e = 0; e < E; ++e) {
+        for (int64_t p = 0; p < P; ++p) {
+            if (ids[p] != e) continue;
+            uint8_t* row = packed + r * ldp;
+            oracle_mx_quantize(x + (p / topk) * K, 1, K, row, row + K);
+            src_pair[r] = (int32_t)p;
+            ++r;
+        }
+        group_end[e] = (int32_t)r;
+    }
+    for (; r < P; ++r) src_pair[r] = -1;
+}
+
 /* ------------------------------------------------------------ transpose --- */
 
 /* out (C, R) = transpose of in (R, C), bytes. */

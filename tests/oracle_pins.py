@@ -433,6 +433,25 @@ def check_group_variants(o, seed=17):
     assert np.array_equal(qc, q3.T) and np.array_equal(sc.view(np.uint32), s3.view(np.uint32))
 
 
+def check_dispatch_pack(o, seed=18):
+    """Dispatch pack against numpy's stable argsort and bincount, and every packed
+    row against the MX quantizer pinned above (codes in front, scales behind)."""
+    rng = np.random.default_rng(seed)
+    for (M, K, topk, E) in [(50, 64, 1, 4), (37, 96, 2, 5), (20, 32, 3, 1)]:
+        x = _random_blocks(rng, M * K // 32).reshape(M, K)
+        ids = rng.integers(-1, E + 1, (M, topk)).astype(np.int32)   # -1 and E are dropped
+        packed, src, ends = o.dispatch_pack(x, ids, E)
+        flat = ids.ravel()
+        keep = np.nonzero((flat >= 0) & (flat < E))[0]
+        order = keep[np.argsort(flat[keep], kind="stable")]
+        n = order.size
+        assert np.array_equal(src[:n], order) and np.all(src[n:] == -1)
+        assert np.array_equal(ends, np.cumsum(np.bincount(flat[keep], minlength=E)))
+        q, s = o.mx_quantize(np.ascontiguousarray(x[order // topk]))
+        assert packed.shape == (M * topk, K + K // 32)
+        assert np.array_equal(packed[:n, :K], q) and np.array_equal(packed[:n, K:], s)
+
+
 def check_group_invariants(o, seed=11):
     rng = np.random.default_rng(seed)
     M, K = 300, 48
@@ -614,7 +633,7 @@ FAST_CHECKS = [
     check_grouped_mm_vs_torch, check_grouped_mm_closed_form, check_grouped_mm_block_scales,
     check_grouped_mm_nan,
     check_mx_rceil_worked_blocks, check_mx_rceil_vs_division, check_mx_axis0_is_transpose,
-    check_group_variants,
+    check_group_variants, check_dispatch_pack,
 ]
 
 

@@ -50,6 +50,13 @@ MUTATIONS = [
     ("group_pow2_rounds_up", "return ldexpf(1.0f, e - 1);", "return ldexpf(1.0f, e);"),
     ("group_pow2_ignored", "if (flags & 1) mult = group_pow2_floor(mult);", "if (flags & 4) mult = group_pow2_floor(mult);"),
     ("group_inverse_not_stored", "stored = (flags & 2) ? one / mult : mult;", "stored = mult;"),
+    ("pack_not_stable", "for (int64_t p = 0; p < P; ++p) {\n            if (ids[p] != e) continue;",
+     "for (int64_t p = P - 1; p >= 0; --p) {\n            if (ids[p] != e) continue;"),
+    ("pack_scales_in_front", "oracle_mx_quantize(x + (p / topk) * K, 1, K, row, row + K);",
+     "oracle_mx_quantize(x + (p / topk) * K, 1, K, row + K / 32, row);"),
+    ("pack_token_index", "oracle_mx_quantize(x + (p / topk) * K, 1, K, row, row + K);",
+     "oracle_mx_quantize(x + (p % M) * K, 1, K, row, row + K);"),
+    ("pack_end_exclusive", "group_end[e] = (int32_t)r;", "group_end[e] = (int32_t)(r > 0 ? r - 1 : 0);"),
     ("group_codes_from_stored_scale", "oracle_group_encode_element(x[r * K + k], mult)",
      "oracle_group_encode_element(x[r * K + k], stored)"),
 ]
