@@ -22,7 +22,8 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libmxq.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
-SOURCES = ["api.hip", "mx_codec.hip", "mx_dim0.hip", "group_scale.hip", "transpose.hip", "grouped_mm.hip"]
+SOURCES = ["api.hip", "mx_codec.hip", "mx_dim0.hip", "dispatch.hip", "group_scale.hip", "transpose.hip",
+           "grouped_mm.hip"]
 ARCH = "gfx950"
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON_FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wextra",

@@ -213,4 +213,66 @@ mxq_status mxq_scaled_grouped_mm(const void* xq_e4m3, const void* xs_e8m0, const
                                              (hipStream_t)stream));
 }
 
+// Dispatch pack limits: pairs and their block histograms fit the int32 indices.
+static mxq_status check_dispatch_sizes(int64_t M, int64_t K, int64_t topk, int64_t E)
+{
+    mxq_status st = check_2d(M, K);
+    if (st != MXQ_OK) return st;
+    if (K <= 0 || K % 256 != 0 || K > ((int64_t)1 << 23)) return MXQ_ERR_SHAPE;
+    if (topk < 1 || topk > 64 || E < 1 || E > mxq::dispatch_max_experts()) return MXQ_ERR_SHAPE;
+    if (M * topk >= ((int64_t)1 << 31) - 256) return MXQ_ERR_SHAPE;
+    if ((M * topk + 255) / 256 * E >= ((int64_t)1 << 31)) return MXQ_ERR_SHAPE;
+    return MXQ_OK;
+}
+
+size_t mxq_dispatch_pack_workspace_bytes(int64_t M, int64_t K, int32_t topk, int32_t E)
+{
+    if (check_dispatch_sizes(M, K, topk, E) != MXQ_OK) return 0;
+    return mxq::dispatch_workspace_bytes(M * topk, E);
+}
+
+mxq_status mxq_dispatch_pack_mx(const void* x_bf16, int64_t M, int64_t K, const int32_t* expert_ids, int32_t topk,
+                                int32_t E, void* packed, int32_t* group_end_offs, int32_t* src_pair,
+                                void* workspace, size_t workspace_bytes, void* stream)
+{
+    mxq_status st = check_dispatch_sizes(M, K, topk, E);
+    if (st != MXQ_OK) return st;
+    if (!group_end_offs || !workspace) return !group_end_offs ? MXQ_ERR_NULL : MXQ_ERR_WORKSPACE;
+    if (M > 0 && (!x_bf16 || !expert_ids || !packed || !src_pair)) return MXQ_ERR_NULL;
+    if (((uintptr_t)group_end_offs & 3u) != 0 || !aligned16(workspace)) return MXQ_ERR_ALIGN;
+    if (M > 0 && (!aligned16(x_bf16) || !aligned16(packed) || ((uintptr_t)expert_ids & 3u) != 0 ||
+                  ((uintptr_t)src_pair & 3u) != 0))
+        return MXQ_ERR_ALIGN;
+    if (workspace_bytes < mxq::dispatch_workspace_bytes(M * topk, E)) return MXQ_ERR_WORKSPACE;
+    hipError_t e = mxq::launch_dispatch_order(expert_ids, M * topk, E, src_pair, group_end_offs, workspace,
+                                              (hipStream_t)stream);
+    if (e == hipSuccess)
+        e = mxq::launch_mx_dispatch_pack(x_bf16, K, src_pair, topk, group_end_offs, E, packed, M * topk,
+                                         (hipStream_t)stream);
+    return hip_status(e);
+}
+
+mxq_status mxq_scaled_grouped_mm_packed(const void* packed, const void* wq_e4m3, const void* ws_e8m0,
+                                        const int32_t* group_end_offs, int64_t M, int64_t N, int64_t K, int32_t G,
+                                        int out_dtype, void* y, void* workspace, size_t workspace_bytes,
+                                        void* stream)
+{
+    mxq_status st = check_grouped_mm_sizes(M, N, K, G);
+    if (st != MXQ_OK) return st;
+    if (K % 512 != 0) return MXQ_ERR_SHAPE;        // 16-byte aligned packed rows
+    if (out_dtype != MXQ_OUT_BF16 && out_dtype != MXQ_OUT_F32) return MXQ_ERR_DTYPE;
+    if (M == 0 || N == 0) return MXQ_OK;
+    if (!packed || !wq_e4m3 || !ws_e8m0 || !group_end_offs || !y) return MXQ_ERR_NULL;
+    if (!aligned16(packed) || !aligned16(wq_e4m3) || !aligned16(ws_e8m0) || !aligned16(y)) return MXQ_ERR_ALIGN;
+    if (((uintptr_t)group_end_offs & 3u) != 0) return MXQ_ERR_ALIGN;
+    const size_t need = mxq::grouped_mm_workspace_bytes(M, N, G);
+    if (!workspace || workspace_bytes < need) return MXQ_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return MXQ_ERR_ALIGN;
+    const uint32_t ldp = (uint32_t)(K + K / 32);
+    const uint8_t* base = static_cast<const uint8_t*>(packed);
+    return hip_status(mxq::launch_grouped_mm_strided(base, base + K, ldp, ldp, wq_e4m3, ws_e8m0, group_end_offs,
+                                                     (int)M, (int)N, (int)K, (int)G, y, out_dtype == MXQ_OUT_F32,
+                                                     workspace, (hipStream_t)stream));
+}
+
 }  // extern "C"

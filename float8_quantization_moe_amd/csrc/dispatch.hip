@@ -1,0 +1,130 @@
+// dispatch.hip -- the order of the dispatch pack: token-slot pairs sorted by
+// expert, stably, on the device (no host synchronisation).
+//
+// "[mxfp8 MoE training] Support mxfp8 all to all in expert parallel", Summary:
+// the all-to-all payload is the MXFP8 encoding of the routed tokens.  Pairs
+// p = t*topk + j with expert ids[p] in [0, E) are placed at
+//   row(p) = start(e) + #{p' < p : ids[p'] == e},
+// a stable counting sort in three passes over 256-pair blocks:
+//   count  per-block histograms (LDS atomics) -> bcount[b][e];
+//   scan   one workgroup turns them into each block's first row per expert
+//          (column prefix sums over blocks, then the experts' starts) and
+//          writes the cumulative end offsets group_end[e];
+//   place  each pair's rank among the earlier pairs of its block with the same
+//          expert (an LDS scan of the block's 256 ids) gives its row.
+// The rows themselves (gather + MX quantize + pack) are written by
+// mx_dispatch_pack_kernel in mx_codec.hip.
+#include "device_common.hpp"
+#include "internal.hpp"
+
+namespace mxq {
+
+constexpr int kDpThreads = 256;          // pairs per block
+constexpr int kDpScanThreads = 1024;
+constexpr int kDpMaxExperts = 1024;
+
+__global__ __launch_bounds__(kDpThreads)
+void dp_count_kernel(const int32_t* __restrict__ ids, int64_t P, int E, int32_t* __restrict__ bcount)
+{
+    __shared__ int hist[kDpMaxExperts];
+    for (int e = (int)threadIdx.x; e < E; e += kDpThreads) hist[e] = 0;
+    __syncthreads();
+    const int64_t p = (int64_t)blockIdx.x * kDpThreads + threadIdx.x;
+    if (p < P) {
+        const int e = ids[p];
+        if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
+    }
+    __syncthreads();
+    for (int e = (int)threadIdx.x; e < E; e += kDpThreads) bcount[(int64_t)blockIdx.x * E + e] = hist[e];
+}
+
+// One workgroup.  Thread (e, seg) = (tid % E, tid / E) owns blocks
+// [seg*len, seg*len + len) of expert e's column, with S = 1024 / E segments.
+__global__ __launch_bounds__(kDpScanThreads)
+void dp_scan_kernel(int32_t* __restrict__ bcount, int nblk, int E, int32_t* __restrict__ group_end)
+{
+    __shared__ int segsum[kDpScanThreads];     // [seg][e], then each segment's start within its column
+    __shared__ int start[kDpMaxExperts];
+    const int S = kDpScanThreads / E;
+    const int len = (nblk + S - 1) / S;
+    const int tid = (int)threadIdx.x;
+    const int e = tid % E, seg = tid / E;
+    const bool mine = seg < S;
+    const int b0 = seg * len, b1 = b0 + len < nblk ? b0 + len : nblk;
+    int sum = 0;
+    if (mine)
+        for (int b = b0; b < b1; ++b) sum += bcount[(int64_t)b * E + e];
+    if (mine) segsum[seg * E + e] = sum;
+    __syncthreads();
+    if (tid < E) {                             // exclusive scan over the segments of column tid
+        int run = 0;
+        for (int sg = 0; sg < S; ++sg) {
+            const int c = segsum[sg * E + tid];
+            segsum[sg * E + tid] = run;
+            run += c;
+        }
+        start[tid] = run;                      // the expert's total, scanned below
+    }
+    __syncthreads();
+    // exclusive scan of the totals over the experts (Hillis-Steele on start[0..E))
+    for (int d = 1; d < E; d <<= 1) {
+        int v = 0;
+        if (tid < E && tid >= d) v = start[tid - d];
+        __syncthreads();
+        if (tid < E) start[tid] += v;
+        __syncthreads();
+    }
+    if (tid < E) group_end[tid] = start[tid];   // inclusive: the end of expert tid
+    __syncthreads();
+    if (mine) {
+        int run = (e > 0 ? start[e - 1] : 0) + segsum[seg * E + e];
+        for (int b = b0; b < b1; ++b) {
+            const int c = bcount[(int64_t)b * E + e];
+            bcount[(int64_t)b * E + e] = run;
+            run += c;
+        }
+    }
+}
+
+__global__ __launch_bounds__(kDpThreads)
+void dp_place_kernel(const int32_t* __restrict__ ids, int64_t P, int E, const int32_t* __restrict__ bbase,
+                     int32_t* __restrict__ src_pair)
+{
+    __shared__ int eid[kDpThreads];
+    const int64_t p = (int64_t)blockIdx.x * kDpThreads + threadIdx.x;
+    int e = p < P ? ids[p] : -1;
+    e = (e >= 0 && e < E) ? e : -1;
+    eid[threadIdx.x] = e;
+    __syncthreads();
+    if (e >= 0) {
+        int rank = 0;
+        for (int i = 0; i < (int)threadIdx.x; ++i) rank += eid[i] == e ? 1 : 0;
+        src_pair[bbase[(int64_t)blockIdx.x * E + e] + rank] = (int32_t)p;
+    }
+}
+
+int dispatch_max_experts() { return kDpMaxExperts; }
+
+size_t dispatch_workspace_bytes(int64_t P, int32_t E)
+{
+    const int64_t nblk = (P + kDpThreads - 1) / kDpThreads;
+    return (size_t)(nblk > 0 ? nblk : 1) * (size_t)E * 4u;
+}
+
+hipError_t launch_dispatch_order(const int32_t* ids, int64_t P, int E, int32_t* src_pair, int32_t* group_end,
+                                 void* workspace, hipStream_t stream)
+{
+    int32_t* bcount = static_cast<int32_t*>(workspace);
+    const int nblk = (int)((P + kDpThreads - 1) / kDpThreads);
+    if (nblk > 0) {
+        hipLaunchKernelGGL(dp_count_kernel, dim3((unsigned)nblk), dim3(kDpThreads), 0, stream, ids, P, E, bcount);
+    }
+    hipLaunchKernelGGL(dp_scan_kernel, dim3(1), dim3(kDpScanThreads), 0, stream, bcount, nblk, E, group_end);
+    if (nblk > 0) {
+        hipLaunchKernelGGL(dp_place_kernel, dim3((unsigned)nblk), dim3(kDpThreads), 0, stream, ids, P, E,
+                           (const int32_t*)bcount, src_pair);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace mxq

@@ -240,15 +240,16 @@ __device__ __forceinline__ int scale_chunk_of(int t, int nk)
 }
 constexpr int kLoadsPerStage = 10;
 
+// (KB: bytes per row of the weight scales; ldxs: of the token scales.)
 __device__ __forceinline__ void issue_chunk(int t, int nk, const v4i& wsr, const v4i& xsr, uint32_t KB,
-                                            uint8_t* lds, int wave, int lane)
+                                            uint32_t ldxs, uint8_t* lds, int wave, int lane)
 {
     const int c = scale_chunk_of(t, nk);
     const uint32_t real = lds_addr(lds + kDataBytes + (c & 1) * 2 * kChunkBytes + 64 * 16 * wave);
     const uint32_t sink = lds_addr(lds + kDataBytes + 2 * 2 * kChunkBytes + 1024 * wave);
-    const uint32_t off = c >= 0 ? (uint32_t)(64 * wave + lane) * KB + (uint32_t)c * 16u : kOOB;
-    dma16(wsr, c >= 0 ? real : sink, off);
-    dma16(xsr, c >= 0 ? real + kChunkBytes : sink, off);
+    const uint32_t row = (uint32_t)(64 * wave + lane);
+    dma16(wsr, c >= 0 ? real : sink, c >= 0 ? row * KB + (uint32_t)c * 16u : kOOB);
+    dma16(xsr, c >= 0 ? real + kChunkBytes : sink, c >= 0 ? row * ldxs + (uint32_t)c * 16u : kOOB);
 }
 
 // Per-wave state of the data loads: the lane's offset of load i (rows
@@ -256,7 +257,8 @@ __device__ __forceinline__ void issue_chunk(int t, int nk, const v4i& wsr, const
 // the wave's first row in slot 0.
 struct DataLoads {
     v4i wr, xr;
-    uint32_t off[4];
+    uint32_t off[4];          // weight rows (stride K)
+    uint32_t offx[4];         // token rows (stride ldx)
     uint32_t lds0;
     int nk;
 };
@@ -267,14 +269,14 @@ __device__ __forceinline__ void issue_data(const DataLoads& d, int t)
 {
     constexpr int i = KL >> 1, op = KL & 1;
     const uint32_t dst = d.lds0 + (uint32_t)(t & (kRing - 1)) * 2 * kTileBytes + op * kTileBytes + 16 * i * kBK;
-    const uint32_t off = t < d.nk ? d.off[i] + (uint32_t)t * kBK : kOOB;
+    const uint32_t off = t < d.nk ? (op == 0 ? d.off[i] : d.offx[i]) + (uint32_t)t * kBK : kOOB;
     dma16(op == 0 ? d.wr : d.xr, dst, off);
 }
 
-__device__ __forceinline__ void issue_stage(int t, int nk, const v4i& wsr, const v4i& xsr, uint32_t KB, uint8_t* lds,
-                                            int wave, int lane, const DataLoads& d)
+__device__ __forceinline__ void issue_stage(int t, int nk, const v4i& wsr, const v4i& xsr, uint32_t KB,
+                                            uint32_t ldxs, uint8_t* lds, int wave, int lane, const DataLoads& d)
 {
-    issue_chunk(t, nk, wsr, xsr, KB, lds, wave, lane);
+    issue_chunk(t, nk, wsr, xsr, KB, ldxs, lds, wave, lane);
     issue_data<0>(d, t); issue_data<1>(d, t); issue_data<2>(d, t); issue_data<3>(d, t);
     issue_data<4>(d, t); issue_data<5>(d, t); issue_data<6>(d, t); issue_data<7>(d, t);
 }
@@ -386,7 +388,7 @@ __device__ __forceinline__ void zero_tile(void* y, int N, int r0, int r1, int n0
 
 template <bool F32OUT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void mm_tile_kernel(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs,
+void mm_tile_kernel(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, uint32_t ldx, uint32_t ldxs,
                     const uint8_t* __restrict__ wq, const uint8_t* __restrict__ wsc, int N, int K, int G,
                     const int* __restrict__ ws, void* __restrict__ y)
 {
@@ -410,9 +412,9 @@ void mm_tile_kernel(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ 
     const int nrows_x = tl.r1 - tl.r0;
     const size_t wrow0 = (size_t)tl.g * (size_t)N + (size_t)n0;
     const v4i wr = make_srd(wq + wrow0 * uK, (uint32_t)nrows_w * uK);
-    const v4i xr = make_srd(xq + (size_t)tl.r0 * uK, (uint32_t)nrows_x * uK);
+    const v4i xr = make_srd(xq + (size_t)tl.r0 * ldx, (uint32_t)nrows_x * ldx);
     const v4i wsr = make_srd(wsc + wrow0 * KB, (uint32_t)nrows_w * KB);
-    const v4i xsr = make_srd(xs + (size_t)tl.r0 * KB, (uint32_t)nrows_x * KB);
+    const v4i xsr = make_srd(xs + (size_t)tl.r0 * ldxs, (uint32_t)nrows_x * ldxs);
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -442,18 +444,19 @@ void mm_tile_kernel(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ 
     for (int i = 0; i < 4; ++i) {
         const int row = 64 * wave + 16 * i + (lane >> 2);
         d.off[i] = (uint32_t)row * uK + ((uint32_t)swz(row, lane & 3) << 4);
+        d.offx[i] = (uint32_t)row * ldx + ((uint32_t)swz(row, lane & 3) << 4);
     }
     int sa[4], sb[4];
-    issue_stage(0, nk, wsr, xsr, KB, lds, wave, lane, d);
-    issue_stage(1, nk, wsr, xsr, KB, lds, wave, lane, d);
-    issue_stage(2, nk, wsr, xsr, KB, lds, wave, lane, d);
+    issue_stage(0, nk, wsr, xsr, KB, ldxs, lds, wave, lane, d);
+    issue_stage(1, nk, wsr, xsr, KB, ldxs, lds, wave, lane, d);
+    issue_stage(2, nk, wsr, xsr, KB, ldxs, lds, wave, lane, d);
     for (int s = 0; s < nk; s += 2) {
         stage_wait();
-        issue_chunk(s + 3, nk, wsr, xsr, KB, lds, wave, lane);
+        issue_chunk(s + 3, nk, wsr, xsr, KB, ldxs, lds, wave, lane);
         load_scales(sa, sb, lds, s, wn, wm, c32, hk);
         mma_stage<0>(acc, lds, s, wn, wm, c32, hk, sa, sb, d, s + 3);
         stage_wait();
-        issue_chunk(s + 4, nk, wsr, xsr, KB, lds, wave, lane);
+        issue_chunk(s + 4, nk, wsr, xsr, KB, ldxs, lds, wave, lane);
         mma_stage<1>(acc, lds, s + 1, wn, wm, c32, hk, sa, sb, d, s + 4);
     }
     // the last three stages' loads read zeros into unused slots; let them land
@@ -512,6 +515,14 @@ hipError_t launch_grouped_mm(const void* xq, const void* xs, const void* wq, con
                              const int32_t* offs, int M, int N, int K, int G, void* y, bool f32_out,
                              void* workspace, hipStream_t stream)
 {
+    return launch_grouped_mm_strided(xq, xs, (uint32_t)K, (uint32_t)K / 32u, wq, wsc, offs, M, N, K, G, y, f32_out,
+                                     workspace, stream);
+}
+
+hipError_t launch_grouped_mm_strided(const void* xq, const void* xs, uint32_t ldx, uint32_t ldxs, const void* wq,
+                                     const void* wsc, const int32_t* offs, int M, int N, int K, int G, void* y,
+                                     bool f32_out, void* workspace, hipStream_t stream)
+{
     const int NC = (N + kBN - 1) / kBN;
     int* ws = static_cast<int*>(workspace);
     hipLaunchKernelGGL(mm_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, offs, G, M, NC, ws);
@@ -520,11 +531,11 @@ hipError_t launch_grouped_mm(const void* xq, const void* xs, const void* wq, con
     const int64_t grid = (mm_slots(M, G) * NC + kXcds - 1) / kXcds * kXcds;
     if (f32_out)
         hipLaunchKernelGGL(mm_tile_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, stream,
-                           static_cast<const uint8_t*>(xq), static_cast<const uint8_t*>(xs),
+                           static_cast<const uint8_t*>(xq), static_cast<const uint8_t*>(xs), ldx, ldxs,
                            static_cast<const uint8_t*>(wq), static_cast<const uint8_t*>(wsc), N, K, G, ws, y);
     else
         hipLaunchKernelGGL(mm_tile_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, stream,
-                           static_cast<const uint8_t*>(xq), static_cast<const uint8_t*>(xs),
+                           static_cast<const uint8_t*>(xq), static_cast<const uint8_t*>(xs), ldx, ldxs,
                            static_cast<const uint8_t*>(wq), static_cast<const uint8_t*>(wsc), N, K, G, ws, y);
     return hipGetLastError();
 }

@@ -9,6 +9,12 @@
 namespace mxq {
 
 hipError_t launch_mx_quantize(const void* x, int64_t M, int64_t K, void* q, void* s, bool rceil, hipStream_t stream);
+hipError_t launch_mx_dispatch_pack(const void* x, int64_t K, int32_t* src_pair, int topk, const int32_t* group_end,
+                                   int E, void* packed, int64_t nrows, hipStream_t stream);
+int dispatch_max_experts();
+size_t dispatch_workspace_bytes(int64_t P, int32_t E);
+hipError_t launch_dispatch_order(const int32_t* ids, int64_t P, int E, int32_t* src_pair, int32_t* group_end,
+                                 void* workspace, hipStream_t stream);
 hipError_t launch_mx_quantize_dim0(const void* x, int64_t M, int64_t K, void* q, void* s, bool rceil,
                                    hipStream_t stream);
 hipError_t launch_mx_dequantize_dim0(const void* q, const void* s, int64_t M, int64_t K, void* y,
@@ -26,6 +32,10 @@ size_t grouped_mm_workspace_bytes(int64_t M, int64_t N, int32_t G);
 hipError_t launch_grouped_mm(const void* xq, const void* xs, const void* wq, const void* ws,
                              const int32_t* offs, int M, int N, int K, int G, void* y, bool f32_out,
                              void* workspace, hipStream_t stream);
+// Token operand with explicit row strides in bytes (codes ldx, scales ldxs; both multiples of 16).
+hipError_t launch_grouped_mm_strided(const void* xq, const void* xs, uint32_t ldx, uint32_t ldxs, const void* wq,
+                                     const void* ws, const int32_t* offs, int M, int N, int K, int G, void* y,
+                                     bool f32_out, void* workspace, hipStream_t stream);
 
 hipError_t launch_transpose_u8(const void* in, int64_t R, int64_t C, void* out, hipStream_t stream);
 

@@ -38,7 +38,8 @@ MXQ_GROUP_INVERSE_SCALE = 2
 EXPORTED = ("mxq_abi_version", "mxq_status_string", "mxq_last_hip_error", "mxq_quantize_mx",
             "mxq_dequantize_mx", "mxq_group_scale_workspace_bytes", "mxq_group_scale_fp8",
             "mxq_transpose_u8", "mxq_grouped_mm_workspace_bytes", "mxq_scaled_grouped_mm",
-            "mxq_quantize_mx_ex", "mxq_dequantize_mx_ex", "mxq_group_scale_fp8_ex")
+            "mxq_quantize_mx_ex", "mxq_dequantize_mx_ex", "mxq_group_scale_fp8_ex",
+            "mxq_dispatch_pack_workspace_bytes", "mxq_dispatch_pack_mx", "mxq_scaled_grouped_mm_packed")
 
 
 class MxqError(RuntimeError):
@@ -86,6 +87,12 @@ def lib() -> ctypes.CDLL:
         L.mxq_transpose_u8.argtypes = [P, i64, i64, P, P]
         L.mxq_grouped_mm_workspace_bytes.restype = sz
         L.mxq_grouped_mm_workspace_bytes.argtypes = [i64, i64, i64, i32]
+        L.mxq_dispatch_pack_workspace_bytes.restype = sz
+        L.mxq_dispatch_pack_workspace_bytes.argtypes = [i64, i64, i32, i32]
+        L.mxq_dispatch_pack_mx.restype = ctypes.c_int
+        L.mxq_dispatch_pack_mx.argtypes = [P, i64, i64, P, i32, i32, P, P, P, P, sz, P]
+        L.mxq_scaled_grouped_mm_packed.restype = ctypes.c_int
+        L.mxq_scaled_grouped_mm_packed.argtypes = [P, P, P, P, i64, i64, i64, i32, ctypes.c_int, P, P, sz, P]
         L.mxq_scaled_grouped_mm.restype = ctypes.c_int
         L.mxq_scaled_grouped_mm.argtypes = [P, P, P, P, P, i64, i64, i64, i32, ctypes.c_int, P, P, sz, P]
         _lib = L
@@ -308,3 +315,52 @@ def scaled_grouped_mm(xq: torch.Tensor, xs: torch.Tensor, wq: torch.Tensor, ws: 
                       device=xq.device)
     mxq_scaled_grouped_mm(xq, xs, wq, ws, group_end_offs, y, wsp, stream)
     return y
+
+
+def mxq_dispatch_pack_workspace_bytes(M: int, K: int, topk: int, E: int) -> int:
+    return int(lib().mxq_dispatch_pack_workspace_bytes(int(M), int(K), int(topk), int(E)))
+
+
+def mxq_dispatch_pack_mx(x: torch.Tensor, expert_ids: torch.Tensor, E: int, packed: torch.Tensor,
+                         group_end_offs: torch.Tensor, src_pair: torch.Tensor, workspace: torch.Tensor,
+                         stream=None) -> None:
+    """x (M, K) bf16, expert_ids (M, topk) int32 -> packed (M*topk, K + K/32) uint8 rows
+    [e4m3 | e8m0] sorted stably by expert, group_end_offs int32[E], src_pair int32[M*topk]."""
+    if x.dim() != 2 or expert_ids.dim() != 2 or expert_ids.shape[0] != x.shape[0]:
+        raise ValueError("x must be (M, K) and expert_ids (M, topk)")
+    M, K = x.shape
+    topk = expert_ids.shape[1]
+    px = _dev(x, "x", torch.bfloat16)
+    pi = _dev(expert_ids, "expert_ids", torch.int32)
+    pp = _dev(packed, "packed", torch.uint8, M * topk * (K + K // 32))
+    pe = _dev(group_end_offs, "group_end_offs", torch.int32, int(E))
+    ps = _dev(src_pair, "src_pair", torch.int32, M * topk)
+    pw = _dev(workspace, "workspace")
+    wbytes = workspace.numel() * workspace.element_size()
+    _check(lib().mxq_dispatch_pack_mx(px, M, K, pi, topk, int(E), pp, pe, ps, pw, wbytes, _stream(stream)),
+           "mxq_dispatch_pack_mx")
+
+
+def mxq_scaled_grouped_mm_packed(packed: torch.Tensor, wq: torch.Tensor, ws: torch.Tensor,
+                                 group_end_offs: torch.Tensor, y: torch.Tensor, workspace: torch.Tensor,
+                                 stream=None) -> None:
+    """packed (M, K + K/32) uint8 token rows [e4m3 | e8m0], wq (G, N, K) / ws (G, N, K/32) ->
+    y (M, N), bf16 or float32 by y's dtype."""
+    if packed.dim() != 2 or wq.dim() != 3 or y.dim() != 2:
+        raise ValueError("packed must be 2-D, wq 3-D (G, N, K), y 2-D (M, N)")
+    G, N, K = wq.shape
+    M = packed.shape[0]
+    if packed.shape[1] != K + K // 32 or tuple(y.shape) != (M, N):
+        raise ValueError("shapes do not match")
+    dt = {torch.bfloat16: MXQ_OUT_BF16, torch.float32: MXQ_OUT_F32}.get(y.dtype)
+    if dt is None:
+        raise TypeError("y must be bfloat16 or float32")
+    pp = _dev(packed, "packed", torch.uint8)
+    pwq = _dev(wq, "wq", torch.uint8)
+    pws = _dev(ws, "ws", torch.uint8, G * N * (K // 32))
+    po = _dev(group_end_offs, "group_end_offs", torch.int32, G)
+    py = _dev(y, "y")
+    pw = _dev(workspace, "workspace")
+    wbytes = workspace.numel() * workspace.element_size()
+    _check(lib().mxq_scaled_grouped_mm_packed(pp, pwq, pws, po, M, N, K, G, dt, py, pw, wbytes, _stream(stream)),
+           "mxq_scaled_grouped_mm_packed")

@@ -295,6 +295,64 @@ mxq_status mxq_scaled_grouped_mm(const void* xq_e4m3, const void* xs_e8m0, const
                                  int64_t N, int64_t K, int32_t G, int out_dtype, void* y,
                                  void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Fused dispatch pack: the all-to-all send buffer of an expert-parallel MoE
+ * layer, built in one call on the device.
+ * Source: "[mxfp8 MoE training] Support mxfp8 all to all in expert parallel",
+ * Summary (the routed tokens are quantized to mxfp8 and exchanged as e4m3 data
+ * plus e8m0 scales).  Sorting the token-expert pairs by expert and packing each
+ * row's two parts together is this library's reading of "quantize straight into
+ * the send buffer": rows for expert e (and so for the rank that owns e) are
+ * contiguous, and one buffer with one split per destination carries both parts.
+ *
+ *   x_bf16          (M, K) bf16 tokens, row-major.
+ *   expert_ids      DEVICE int32 (M, topk): expert of slot j of token t at
+ *                   [t*topk + j].  Ids outside [0, E) drop that pair.
+ *   packed          (M*topk, K + K/32) uint8 output rows: row r holds the MX
+ *                   encoding (as mxq_quantize_mx) of token src_pair[r] / topk,
+ *                   its K e4m3 codes then its K/32 e8m0 scales.
+ *   group_end_offs  DEVICE int32[E] output: cumulative end row of each expert
+ *                   (the group offsets mxq_scaled_grouped_mm_packed and the group
+ *                   scaling take).
+ *   src_pair        DEVICE int32[M*topk] output: the pair index t*topk + j of
+ *                   each row (for the return trip); -1 for rows at or past
+ *                   group_end_offs[E-1].
+ *   workspace       DEVICE scratch of mxq_dispatch_pack_workspace_bytes(M, K,
+ *                   topk, E) bytes, 16-B aligned, no initialisation needed.
+ *
+ * Order: by expert, and within an expert by pair index (a stable sort), so the
+ * result is deterministic.  Rows at or past the last end are not written.
+ * Requires K % 256 == 0 (8-byte aligned rows), 0 < K <= 2^23, 1 <= topk <= 64,
+ * 1 <= E <= 1024, M*topk < 2^31 - 256 (MXQ_ERR_SHAPE).  x and packed 16-byte
+ * aligned, the int32 arrays 4-byte aligned (MXQ_ERR_ALIGN).  M == 0 writes
+ * only group_end_offs (all zero).
+ */
+size_t mxq_dispatch_pack_workspace_bytes(int64_t M, int64_t K, int32_t topk, int32_t E);
+mxq_status mxq_dispatch_pack_mx(const void* x_bf16, int64_t M, int64_t K, const int32_t* expert_ids,
+                                int32_t topk, int32_t E, void* packed, int32_t* group_end_offs,
+                                int32_t* src_pair, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+/*
+ * mxq_scaled_grouped_mm with the token operand read straight from a packed
+ * buffer as mxq_dispatch_pack_mx writes it (rows of K e4m3 codes followed by
+ * K/32 e8m0 scales, row stride K + K/32 bytes): the receiver multiplies the
+ * payload as received, with no dequantization and no unpacking.
+ * Source: "[mxfp8 MoE training] Support mxfp8 all to all in expert parallel",
+ * Summary (the receiver of the mxfp8 payload), and the grouped product of
+ * mxq_scaled_grouped_mm.
+ *
+ *   packed  (M, K + K/32) uint8, 16-byte aligned.  Everything else, the result
+ *           and every error as for mxq_scaled_grouped_mm (same workspace size),
+ *           plus K % 512 == 0 (MXQ_ERR_SHAPE) so that every packed row is
+ *           16-byte aligned.  Bit-identical to mxq_scaled_grouped_mm on the
+ *           unpacked codes and scales.
+ */
+mxq_status mxq_scaled_grouped_mm_packed(const void* packed, const void* wq_e4m3, const void* ws_e8m0,
+                                        const int32_t* group_end_offs, int64_t M, int64_t N, int64_t K,
+                                        int32_t G, int out_dtype, void* y, void* workspace,
+                                        size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -30,7 +30,8 @@ def test_header_declares_the_entry_points():
     for n in ("mxq_quantize_mx", "mxq_dequantize_mx", "mxq_group_scale_fp8",
               "mxq_group_scale_workspace_bytes", "mxq_transpose_u8", "mxq_abi_version",
               "mxq_grouped_mm_workspace_bytes", "mxq_scaled_grouped_mm", "mxq_quantize_mx_ex",
-              "mxq_dequantize_mx_ex", "mxq_group_scale_fp8_ex"):
+              "mxq_dequantize_mx_ex", "mxq_group_scale_fp8_ex", "mxq_dispatch_pack_workspace_bytes",
+              "mxq_dispatch_pack_mx", "mxq_scaled_grouped_mm_packed"):
         assert n in names
 
 
@@ -131,6 +132,46 @@ def test_group_scale_argument_errors(L):
     assert fx(A, 512, 252, A, 4, 0, 3, A, A, A, ws, S) == 2
     assert fx(A, 512, 256, A, 4, 0, 3, A, A, A, ws - 1, S) == 5
     assert fx(A, 512, 0, A, 4, 0, 3, A, A, A, ws, S) == 0
+
+
+def test_dispatch_pack_argument_errors(L):
+    S = 0
+    wb = L.mxq_dispatch_pack_workspace_bytes
+    ws = wb(1000, 5120, 1, 16)
+    assert ws == 4 * 16 * 4                                   # 4 blocks of 256 pairs x 16 experts
+    assert wb(1000, 5120, 2, 16) == 8 * 16 * 4
+    assert wb(1000, 5000, 1, 16) == 0                         # K % 256
+    assert wb(1000, 0, 1, 16) == 0                            # K == 0
+    assert wb(1000, 5120, 0, 16) == 0 and wb(1000, 5120, 65, 16) == 0   # topk
+    assert wb(1000, 5120, 1, 0) == 0 and wb(1000, 5120, 1, 1025) == 0   # experts
+    assert wb(1 << 31, 256, 1, 4) == 0                        # pairs beyond int32
+    f = L.mxq_dispatch_pack_mx
+    assert f(A, 1000, 5000, A, 1, 16, A, A, A, A, ws, S) == 2
+    assert f(A, 1000, 5120, A, 1, 2000, A, A, A, A, ws, S) == 2
+    assert f(A, 1000, 5120, A, 1, 16, A, 0, A, A, ws, S) == 1      # null group ends
+    assert f(0, 1000, 5120, A, 1, 16, A, A, A, A, ws, S) == 1      # null x
+    assert f(A, 1000, 5120, 0, 1, 16, A, A, A, A, ws, S) == 1      # null ids
+    assert f(A, 1000, 5120, A, 1, 16, 0, A, A, A, ws, S) == 1      # null packed
+    assert f(A, 1000, 5120, A, 1, 16, A, A, 0, A, ws, S) == 1      # null src_pair
+    assert f(A, 1000, 5120, A, 1, 16, A, A, A, 0, ws, S) == 5      # no workspace
+    assert f(A, 1000, 5120, A, 1, 16, A, A, A, A, ws - 1, S) == 5
+    assert f(A + 4, 1000, 5120, A, 1, 16, A, A, A, A, ws, S) == 3  # misaligned x
+    assert f(A, 1000, 5120, A + 2, 1, 16, A, A, A, A, ws, S) == 3  # misaligned ids
+    assert f(A, 1000, 5120, A, 1, 16, A + 8, A, A, A, ws, S) == 3  # misaligned packed
+    assert f(A, 1000, 5120, A, 1, 16, A, A + 1, A, A, ws, S) == 3  # misaligned group ends
+
+
+def test_grouped_mm_packed_argument_errors(L):
+    S = 0
+    need = L.mxq_grouped_mm_workspace_bytes(300, 256, 5120, 4)
+    g = L.mxq_scaled_grouped_mm_packed
+    assert g(A, A, A, A, 300, 256, 5120 - 128, 4, 0, A, A, need, S) == 2    # K % 512
+    assert g(A, A, A, A, 300, 250, 5120, 4, 0, A, A, need, S) == 2          # N % 8
+    assert g(A, A, A, A, 300, 256, 5120, 4, 2, A, A, need, S) == 8          # dtype
+    assert g(0, A, A, A, 300, 256, 5120, 4, 0, A, A, need, S) == 1
+    assert g(A + 4, A, A, A, 300, 256, 5120, 4, 0, A, A, need, S) == 3
+    assert g(A, A, A, A, 300, 256, 5120, 4, 0, A, A, need - 1, S) == 5
+    assert g(0, 0, 0, 0, 0, 256, 5120, 4, 0, 0, 0, 0, S) == 0               # M == 0: no-op
 
 
 def test_transpose_argument_errors(L):

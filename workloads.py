@@ -109,6 +109,16 @@ def zipf_group_ends(M: int, G: int, alpha: float = ZIPF_ALPHA, seed: int = 1) ->
     return ends_from_sizes(zipf_group_sizes(M, G, alpha, seed))
 
 
+def routed_expert_ids(M: int, E: int, topk: int = 1, alpha: float = ZIPF_ALPHA, seed: int = 1) -> np.ndarray:
+    """(M, topk) int32 expert ids, Zipf(alpha) over E experts (expert 0 hottest): the
+    same draw as zipf_group_sizes, so for topk = 1 the ids' bincount is exactly those
+    group sizes (the dispatch pack of these ids yields zipf_group_ends)."""
+    p = torch.arange(1, E + 1, dtype=torch.float64) ** (-alpha)
+    p = p / p.sum()
+    assign = torch.multinomial(p, M * topk, replacement=True, generator=_gen(seed))
+    return assign.numpy().astype(np.int32).reshape(M, topk)
+
+
 def random_bf16_bits(shape, seed: int, finite_only: bool = True) -> np.ndarray:
     """Uniformly random bf16 bit patterns (all exponents), optionally finite only."""
     rng = np.random.default_rng(seed)
