@@ -247,6 +247,31 @@ def bench_grouped_mm(args, dev, stream, x_host, ends, W, mxq, np, torch):
     torch.cuda.synchronize()
     times = sorted(e[0].elapsed_time(e[1]) * 1e3 for e in evs)
     med = times[len(times) // 2]
+
+    # the same product on the packed dispatch payload (tokens routed top-1 by the
+    # Zipf draw whose group sizes these are), packed by mxq_dispatch_pack_mx
+    x_dev = x_host.to(dev)
+    ids = torch.from_numpy(W.routed_expert_ids(M, G, topk=1, seed=1)).to(dev)
+    packed = torch.empty((M, K + K // 32), dtype=torch.uint8, device=dev)
+    pends = torch.empty(G, dtype=torch.int32, device=dev)
+    src = torch.empty(M, dtype=torch.int32, device=dev)
+    dws = torch.empty(mxq.mxq_dispatch_pack_workspace_bytes(M, K, 1, G), dtype=torch.uint8, device=dev)
+    mxq.mxq_dispatch_pack_mx(x_dev, ids, G, packed, pends, src, dws, stream)
+    torch.cuda.synchronize()
+    del x_dev
+    same_groups = bool(np.array_equal(pends.cpu().numpy(), ends))
+    for i in range(2):
+        mxq.mxq_scaled_grouped_mm_packed(packed, wq3, ws3, pends, y, wsp, stream)
+    torch.cuda.synchronize()
+    pevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for i in range(reps):
+        pevs[i][0].record(stream)
+        mxq.mxq_scaled_grouped_mm_packed(packed, wq3, ws3, pends, y, wsp, stream)
+        pevs[i][1].record(stream)
+    torch.cuda.synchronize()
+    ptimes = sorted(e[0].elapsed_time(e[1]) * 1e3 for e in pevs)
+    pmed = ptimes[len(ptimes) // 2]
+    del packed, src, dws, ids
     rows = int(ends[-1])                                  # routed rows (all of them here)
     flops = 2.0 * rows * N * K
     tflops = flops / (med * 1e6)
@@ -258,6 +283,10 @@ def bench_grouped_mm(args, dev, stream, x_host, ends, W, mxq, np, torch):
         "roofline": {"bound": "mfma", "kernel": "mm_tile_kernel", "achieved": round(tflops, 1),
                      "peak": MFMA_FP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / MFMA_FP8_PEAK_TFLOPS, 4),
                      "flops_per_launch": flops, "timed": "median of per-launch events (plan + tile kernels)"},
+        "packed_payload": {"median_us": round(pmed, 1), "TFLOPs": round(2.0 * rows * N * K / (pmed * 1e6), 1),
+                           "frac": round(2.0 * rows * N * K / (pmed * 1e6) / MFMA_FP8_PEAK_TFLOPS, 4),
+                           "same_groups_as_above": same_groups,
+                           "what": "mxq_scaled_grouped_mm_packed on the mxq_dispatch_pack_mx rows"},
         "weight_quantize_us": round(wquant_us, 1),
         "operand_bytes": M * K * (1 + 1 / 32) + G * N * K * (1 + 1 / 32) + 2 * M * N,
     }
@@ -398,6 +427,29 @@ def main():
         variants[name] = {"avg_us": round(us, 2), "algorithmic_bytes": nbytes, "GBps": round(nbytes / (us * 1e3), 1),
                           "frac_of_peak": round(nbytes / (us * 1e3) / HBM_PEAK_GBPS, 4),
                           "shape": [M1, K1] if name.startswith("mx_") else [M2, K2]}
+    # the fused dispatch pack at the dispatch shape: (65536, 5120) routed top-1 over 16 Zipf experts
+    ids1 = torch.from_numpy(W.routed_expert_ids(M1, G_ROW, topk=1, seed=1)).to(dev)
+    pk1 = torch.empty((M1, K1 + K1 // 32), dtype=torch.uint8, device=dev)
+    pe1 = torch.empty(G_ROW, dtype=torch.int32, device=dev)
+    ps1 = torch.empty(M1, dtype=torch.int32, device=dev)
+    pw1 = torch.empty(mxq.mxq_dispatch_pack_workspace_bytes(M1, K1, 1, G_ROW), dtype=torch.uint8, device=dev)
+    fn = lambda i: mxq.mxq_dispatch_pack_mx(sets[i % len(sets)].x1, ids1, G_ROW, pk1, pe1, ps1, pw1, stream)
+    for i in range(2):
+        fn(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for r in range(reps):
+        fn(r)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    nb = mx_bytes(M1, K1) + M1 * 4 * 2               # + the ids read and the source indices written
+    variants["dispatch_pack_top1_e16"] = {"avg_us": round(us, 2), "algorithmic_bytes": nb,
+                                          "GBps": round(nb / (us * 1e3), 1),
+                                          "frac_of_peak": round(nb / (us * 1e3) / HBM_PEAK_GBPS, 4),
+                                          "shape": [M1, K1], "what": "sort by expert + gather + MX quantize + pack"}
+    del ids1, pk1, pe1, ps1, pw1
     # the other operand of the weight-gradient GEMM: dY (16640, 8192), 16 groups, column-major
     dy = [torch.empty((M2, WGRAD_N), dtype=torch.bfloat16, device=dev).normal_() for _ in range(min(2, len(sets)))]
     qdy = torch.empty((WGRAD_N, M2), dtype=torch.uint8, device=dev)

@@ -135,42 +135,39 @@ void mx_dequantize_kernel(const uint2* __restrict__ q, const uint8_t* __restrict
 // is the MX encoding of token src_pair[r] / topk, its K codes followed by its
 // K/32 scales, exactly the bytes mxq_quantize_mx writes for that token.  Rows
 // at or past the last expert's end are not written; their src_pair becomes -1.
-// The same flat pass as mx_quantize_kernel over the packed rows' chunks, with
-// the token row gathered through src_pair (one contiguous 16-byte load per
-// lane, 640 lanes per row at K = 5120).
-static unsigned codec_grid(int64_t nchunks);
-
+// One workgroup per packed row (grid-stride over rows): the source token is one
+// uniform load, and the row's K/8 chunks go through the codec's quantizer
+// kCodecThreads * kCodecUnroll at a time (a quad of lanes per 32-block).
 __global__ __launch_bounds__(kCodecThreads)
-void mx_dispatch_pack_kernel(const uint4* __restrict__ x, int64_t K8, int32_t* src_pair, int topk,
+void mx_dispatch_pack_kernel(const uint4* __restrict__ x, int K8, int32_t* src_pair, int topk,
                              const int32_t* __restrict__ group_end, int E, uint8_t* __restrict__ packed,
-                             int64_t ldp, int64_t nchunks)
+                             int64_t ldp, int64_t nrows)
 {
     const int64_t total = group_end[E - 1];
-    const int64_t K = K8 * 8;
-    const int64_t per_block = (int64_t)kCodecThreads * kCodecUnroll;
-    for (int64_t base = (int64_t)blockIdx.x * per_block + threadIdx.x; base < nchunks;
-         base += (int64_t)gridDim.x * per_block) {
-        uint4 v[kCodecUnroll];
-        int64_t row[kCodecUnroll], cc[kCodecUnroll];
-#pragma unroll
-        for (int u = 0; u < kCodecUnroll; ++u) {
-            const int64_t c = base + (int64_t)u * kCodecThreads;
-            row[u] = c / K8;
-            cc[u] = c - row[u] * K8;
-            const bool in = c < nchunks && row[u] < total;
-            v[u] = in ? load_nt(x + (int64_t)(src_pair[row[u]] / topk) * K8 + cc[u]) : make_uint4(0, 0, 0, 0);
+    const int64_t K = (int64_t)K8 * 8;
+    for (int64_t r = blockIdx.x; r < nrows; r += gridDim.x) {
+        if (r >= total) {                              // uniform
+            if (threadIdx.x == 0) src_pair[r] = -1;
+            continue;
         }
+        const uint4* xr = x + (int64_t)(src_pair[r] / topk) * K8;
+        uint8_t* dst = packed + r * ldp;
+        for (int c0 = 0; c0 < K8; c0 += kCodecThreads * kCodecUnroll) {
+            uint4 v[kCodecUnroll];
 #pragma unroll
-        for (int u = 0; u < kCodecUnroll; ++u) {
-            const int64_t c = base + (int64_t)u * kCodecThreads;
-            uint32_t code;
-            const uint2 out = quantize_chunk<false>(v[u], &code);   // whole quads lie in one row
-            if (c < nchunks && row[u] < total) {
-                uint8_t* dst = packed + row[u] * ldp;
-                store_nt(out, (uint2*)(dst + cc[u] * 8));
-                if ((threadIdx.x & 3) == 0) dst[K + (cc[u] >> 2)] = (uint8_t)code;
-            } else if (c < nchunks && cc[u] == 0) {
-                src_pair[row[u]] = -1;
+            for (int u = 0; u < kCodecUnroll; ++u) {
+                const int cc = c0 + u * kCodecThreads + (int)threadIdx.x;
+                v[u] = cc < K8 ? load_nt(xr + cc) : make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int u = 0; u < kCodecUnroll; ++u) {
+                const int cc = c0 + u * kCodecThreads + (int)threadIdx.x;
+                uint32_t code;
+                const uint2 out = quantize_chunk<false>(v[u], &code);   // whole quads are in or out (K8 % 4 == 0)
+                if (cc < K8) {
+                    store_nt(out, (uint2*)(dst + (int64_t)cc * 8));
+                    if ((threadIdx.x & 3) == 0) dst[K + (cc >> 2)] = (uint8_t)code;
+                }
             }
         }
     }
@@ -179,11 +176,10 @@ void mx_dispatch_pack_kernel(const uint4* __restrict__ x, int64_t K8, int32_t* s
 hipError_t launch_mx_dispatch_pack(const void* x, int64_t K, int32_t* src_pair, int topk, const int32_t* group_end,
                                    int E, void* packed, int64_t nrows, hipStream_t stream)
 {
-    const int64_t K8 = K / 8;
-    const int64_t nchunks = nrows * K8;
-    if (nchunks == 0) return hipSuccess;
-    hipLaunchKernelGGL(mx_dispatch_pack_kernel, dim3(codec_grid(nchunks)), dim3(kCodecThreads), 0, stream,
-                       (const uint4*)x, K8, src_pair, topk, group_end, E, (uint8_t*)packed, K + K / 32, nchunks);
+    if (nrows == 0 || K == 0) return hipSuccess;
+    const unsigned grid = (unsigned)(nrows < (1 << 22) ? nrows : (1 << 22));
+    hipLaunchKernelGGL(mx_dispatch_pack_kernel, dim3(grid), dim3(kCodecThreads), 0, stream, (const uint4*)x,
+                       (int)(K / 8), src_pair, topk, group_end, E, (uint8_t*)packed, K + K / 32, nrows);
     return hipGetLastError();
 }
 
