@@ -91,7 +91,7 @@ def parse_args():
     return p.parse_args()
 
 
-COUNTER_SOURCES = ["mx_codec.hip", "device_common.hpp"]
+COUNTER_SOURCES = ["mx_codec.hip", "mx_dim0.hip", "device_common.hpp"]
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 COPY_BYTES = 1 << 30       # the 1 GiB device copies of the streaming-ceiling leg
 
@@ -105,18 +105,26 @@ def ingest_counters(stats_csv, fetch_csv, write_csv, sq_csv=None, commands=""):
     import collections
     import statistics
 
+    def norm(name):                               # "void mxq::k<false>(...)" -> "mxq::k<false>"
+        name = name.split("(")[0]
+        return name[5:] if name.startswith("void ") else name
+
     def per_kernel(path, field="Counter_Value"):
         agg = collections.defaultdict(list)
         for r in csv.DictReader(open(path)):
-            agg[r["Kernel_Name"].split("(")[0]].append(float(r[field]))
+            agg[norm(r["Kernel_Name"])].append(float(r[field]))
         return agg
 
     fetch, write = per_kernel(fetch_csv), per_kernel(write_csv)
     f_copy = max(fetch[COPY_KERNEL]) * 1024.0
     w_copy = max(write[COPY_KERNEL]) * 1024.0
     f_scale, w_scale = COPY_BYTES / f_copy, COPY_BYTES / w_copy
-    stats = {r["Name"].split("(")[0]: r for r in csv.DictReader(open(stats_csv))}
-    algo = {"mxq::mx_quantize_kernel": mx_bytes(*DISPATCH), "mxq::mx_dequantize_kernel": mx_bytes(*DISPATCH),
+    stats = {norm(r["Name"]): r for r in csv.DictReader(open(stats_csv))}
+    mxb = mx_bytes(*DISPATCH)
+    algo = {"mxq::mx_quantize_kernel<false>": mxb, "mxq::mx_quantize_kernel<true>": mxb,
+            "mxq::mx_dequantize_kernel": mxb, "mxq::mx_quantize_dim0_kernel<false>": mxb,
+            "mxq::mx_quantize_dim0_kernel<true>": mxb, "mxq::mx_dequantize_dim0_kernel": mxb,
+            "mxq::mx_dispatch_pack_kernel": mxb + 4 * DISPATCH[0],
             "mxq::transpose_u8_kernel": transpose_bytes(*TOKENS)}
     lines = ["# HBM traffic per dispatch, hot-path step (dispatch payload 65536x5120, tokens 16640x5120)", "",
              "Commands (from the repository root):", "", "```", commands.strip(), "```", "",
@@ -144,11 +152,14 @@ def ingest_counters(stats_csv, fetch_csv, write_csv, sq_csv=None, commands=""):
         if k not in fetch or k not in write:
             return None
         return statistics.mean(fetch[k]) * 1024 * f_scale + statistics.mean(write[k]) * 1024 * w_scale
-    calls = [("group scaling G=16 row-major (plan + hold)", ["void mxq::group_plan_kernel<128>", "void mxq::group_hold_kernel<0>"],
+    calls = [("group scaling G=16 row-major (plan + hold)", ["mxq::group_plan_kernel<128>", "mxq::group_hold_kernel<0>"],
               group_bytes(TOKENS[0], TOKENS[1], 16)),
              ("group scaling G=128 column-major (plan + amax + finalize + quantize)",
-              ["void mxq::group_plan_kernel<128>", "void mxq::group_amax_kernel<1>", "mxq::group_finalize_kernel",
-               "mxq::group_quant_col_blocks_kernel"], group_bytes(TOKENS[0], TOKENS[1], 128))]
+              ["mxq::group_plan_kernel<128>", "mxq::group_amax_kernel<1>", "mxq::group_finalize_kernel",
+               "mxq::group_quant_col_blocks_kernel"], group_bytes(TOKENS[0], TOKENS[1], 128)),
+             ("dispatch pack, top-1 over 16 experts (count + scan + place + pack)",
+              ["mxq::dp_count_kernel", "mxq::dp_scan_kernel", "mxq::dp_place_kernel", "mxq::mx_dispatch_pack_kernel"],
+              mx_bytes(*DISPATCH) + 8 * DISPATCH[0])]
     lines += ["", "Whole calls (sum of the kernels each call launches):", "",
               "| call | scaled HBM bytes | algorithmic bytes | ratio |", "|---|---|---|---|"]
     for name, ks, a in calls:
@@ -519,7 +530,7 @@ def main():
     # --------------------------------------------------- dominant kernel ---
     # the single-kernel call that takes the longest; its launch is bracketed by
     # events on the stream it runs on
-    dom_kernel = {"mx_quantize": "mx_quantize_kernel", "mx_dequantize": "mx_dequantize_kernel"}[dom]
+    dom_kernel = {"mx_quantize": "mx_quantize_kernel<false>", "mx_dequantize": "mx_dequantize_kernel"}[dom]
     achieved = call_bytes[dom] / (dom_us * 1e3)
     traffic = None
     traffic_note = "no counter file"
@@ -564,6 +575,30 @@ def main():
         b = sets[(args.warmup + args.steps - 1) % len(sets)]
         same_mx = (np.array_equal(b.q1[:r1].cpu().numpy(), q) and np.array_equal(b.s1[:r1].cpu().numpy(), s)
                    and np.array_equal(W.bf16_bits(b.y1[:r1].cpu()), y))
+        # the same oracle calls on all available host threads, rows split statically
+        # (the oracle's C code releases the GIL inside each call); group scaling is
+        # split by columns, which keeps every group's rows together
+        from concurrent.futures import ThreadPoolExecutor
+        nthr = max(1, min(ncpu or 1, 16))
+        def rows_of(n):
+            step = -(-n // nthr)
+            return [(a, min(n, a + step)) for a in range(0, n, step)]
+        def cols_of(n):
+            step = max(8, -(-n // nthr) // 8 * 8)
+            return [(a, min(n, a + step)) for a in range(0, n, step)]
+        def mx_part(ab):
+            qq, ss = oracle.mx_quantize(np.ascontiguousarray(xb1[ab[0]:ab[1]]))
+            oracle.mx_dequantize(qq, ss)
+        def grp_part(ab):
+            xs_ = np.ascontiguousarray(xb2[:, ab[0]:ab[1]])
+            oracle.group_scale(xs_, e16, oracle.LAYOUT_ROW)
+            gq, _ = oracle.group_scale(xs_, e128, oracle.LAYOUT_COL)
+            oracle.transpose_u8(gq)
+        t2 = time.perf_counter()
+        with ThreadPoolExecutor(nthr) as ex:
+            list(ex.map(mx_part, rows_of(r1)))
+            list(ex.map(grp_part, cols_of(K2)))
+        t3 = time.perf_counter()
         cpu_baseline = {
             "value": round(sample_bytes / ((t1 - t0) * 1e9), 3), "unit": "GB/s", "cores": 1,
             "kind": "oracle", "seconds": round(t1 - t0, 2),
@@ -572,6 +607,9 @@ def main():
                        f"over wall time"),
             "cpu_model": model, "host_cpus_available": ncpu,
             "mx_sample_matches_gpu": bool(same_mx),
+            "all_cores": {"value": round(sample_bytes / ((t3 - t2) * 1e9), 3), "unit": "GB/s", "cores": nthr,
+                          "seconds": round(t3 - t2, 2),
+                          "split": "MX rows, group-scaling columns, statically over the threads"},
         }
 
     props = torch.cuda.get_device_properties(0)
