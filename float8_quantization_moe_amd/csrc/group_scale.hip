@@ -1156,10 +1156,11 @@ static hipError_t launch_layout(const void* x, int M, int K, const int32_t* offs
     const unsigned long long timeout_ticks =
         (unsigned long long)(rate_khz > 0 ? rate_khz : 100000) * (unsigned long long)wait_us / 1000ull;
     // MXQ_GROUP_MODE=hold|twopass picks the method.  Default: hold, except for
-    // column-major output with many groups, where the hold kernel's tiles cut at
-    // group boundaries split too many output lines (measured crossover at about
-    // one group per two 128-row blocks).
-    bool twopass = LAYOUT == 1 && 2 * (int64_t)G >= (M + 127) / 128;
+    // column-major output with more than a few groups, where the hold kernel's
+    // tiles cut at group boundaries split too many output lines (measured at
+    // 16640 x 5120: hold wins at 16 groups, two-pass from 32 on, so the switch is
+    // at about one group per five 128-row blocks).  Row-major output always holds.
+    bool twopass = LAYOUT == 1 && 5 * (int64_t)G >= (M + 127) / 128;
     if (const char* v = getenv("MXQ_GROUP_MODE")) {
         if (strcmp(v, "twopass") == 0) twopass = true;
         if (strcmp(v, "hold") == 0) twopass = false;
