@@ -82,8 +82,8 @@ def parse_args():
     p.add_argument("--rotate", type=int, default=4, help="independent buffer sets cycled through")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-gemm", action="store_true", help="skip the grouped GEMM leg")
-    p.add_argument("--cpu-mx-rows", type=int, default=16384, help="dispatch rows in the CPU sample")
-    p.add_argument("--cpu-group-rows", type=int, default=8320, help="token rows in the CPU sample")
+    p.add_argument("--cpu-mx-rows", type=int, default=49152, help="dispatch rows in the CPU sample")
+    p.add_argument("--cpu-group-rows", type=int, default=16640, help="token rows in the CPU sample")
     p.add_argument("--ingest-counters", nargs="+", metavar="CSV",
                    help="turn rocprofv3 outputs of this script (kernel stats, FETCH_SIZE and WRITE_SIZE "
                         "counter collections) into the summaries under profiles/ and exit")
@@ -602,9 +602,10 @@ def main():
         cpu_baseline = {
             "value": round(sample_bytes / ((t1 - t0) * 1e9), 3), "unit": "GB/s", "cores": 1,
             "kind": "oracle", "seconds": round(t1 - t0, 2),
-            "sample": (f"same five calls on the first {r1} of {M1} dispatch rows and the first {r2} of {M2} "
-                       f"token rows (group offsets cut at {r2}); one thread; algorithmic bytes of the sample "
-                       f"over wall time"),
+            "sample": (f"same five calls on the first {r1} of {M1} dispatch rows and "
+                       + (f"all {M2} token rows" if r2 == M2 else
+                          f"the first {r2} of {M2} token rows (group offsets cut at {r2})")
+                       + "; one thread; algorithmic bytes of the sample over wall time"),
             "cpu_model": model, "host_cpus_available": ncpu,
             "mx_sample_matches_gpu": bool(same_mx),
             "all_cores": {"value": round(sample_bytes / ((t3 - t2) * 1e9), 3), "unit": "GB/s", "cores": nthr,
