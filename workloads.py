@@ -76,6 +76,21 @@ def lognormal_rows(M: int, K: int, seed: int = 0) -> torch.Tensor:
     return x
 
 
+def device_tokens(M: int, K: int, seed: int = 0, chunk_rows: int = 32768) -> torch.Tensor:
+    """As lognormal_rows (N(0, 1) times a per-row lognormal(0, 1) factor), but drawn
+    on the current GPU in row chunks and cast to bf16 there: for sizes too large to
+    draw and copy from the host.  Both sides read the same device bytes."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    x = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+    for a in range(0, M, chunk_rows):
+        b = min(M, a + chunk_rows)
+        c = torch.randn((b - a, K), generator=g, device="cuda")
+        c *= torch.exp(torch.randn((b - a, 1), generator=g, device="cuda"))
+        x[a:b] = c.to(torch.bfloat16)
+    return x
+
+
 def dispatch_payload(M: int = DISPATCH_SHAPE[0], K: int = DISPATCH_SHAPE[1], seed: int = 0,
                      outlier_frac: float = 0.001, outlier_mult: float = 100.0,
                      zero_row_frac: float = 0.01) -> torch.Tensor:
