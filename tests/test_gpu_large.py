@@ -8,7 +8,9 @@ transform): the same calls at (266240, 8192) bf16, 2.18e9 elements, whose
 element offset 2^31 falls on row 262144.  The oracle checks sampled rows of the
 MX codec (row blocks are independent) and whole sampled columns of the group
 scaling (columns are independent); the transform is checked in full against
-the row-major output.
+the row-major output.  The grouped product writes a (266240, 8192) output, also
+past 2^31 elements, checked at sampled rows and columns against the
+double-precision oracle with the bounds of test_gpu_grouped_mm.
 """
 import numpy as np
 import pytest
@@ -16,6 +18,7 @@ import torch
 
 import gpu_util as U
 import oracle
+import test_gpu_grouped_mm as GM
 import workloads as W
 from float8_quantization_moe_amd import mxq
 
@@ -129,3 +132,30 @@ def test_group_scaling_and_transform_past_2_31_elements(x, mode, monkeypatch):
     torch.cuda.synchronize()
     assert tg.guard_intact()
     assert torch.equal(tg.t, qr.t), "transform of the column-major codes differs from the row-major codes"
+
+
+def test_grouped_mm_output_past_2_31_elements():
+    """Tokens (266240, 256) in 16 Zipf groups times 16 experts' (8192, 256)
+    weights: the bf16 output's element offset 2^31 falls on row 262144."""
+    Mx, N, Kx, G = M, 8192, 256, 16
+    assert torch.cuda.is_available(), "these tests need an MI355X"
+    print(f"grouped mm M={Mx} N={N} K={Kx} G={G}", flush=True)
+    ends = W.zipf_group_ends(Mx, G)
+    xq, xs = U.oracle_mx_quantize(W.bf16_bits(W.moe_tokens(Mx, Kx, seed=22)))
+    wq, ws = U.oracle_mx_quantize(W.bf16_bits(W.expert_weights(G, N, Kx, seed=23)).reshape(G * N, Kx))
+    wq, ws = wq.reshape(G, N, Kx), ws.reshape(G, N, Kx // 32)
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    wsp = torch.empty(mxq.mxq_grouped_mm_workspace_bytes(Mx, N, Kx, G), dtype=torch.uint8, device="cuda")
+    yg = U.Guarded(Mx * N, torch.bfloat16, (Mx, N))
+    mxq.mxq_scaled_grouped_mm(d(xq), d(xs), d(wq), d(ws), d(ends), yg.t, wsp)
+    torch.cuda.synchronize()
+    assert yg.guard_intact(), "wrote past the end of y"
+    rng = np.random.default_rng(24)
+    boundary = (1 << 31) // N
+    rows = np.array(sorted(set(GM._sample_rows(ends, Mx, rng).tolist() + [boundary - 1, boundary, Mx - 1])), np.int64)
+    cols = np.array(sorted(set([0, 1, 255, 256, 4095, 4096, N - 1] + rng.integers(0, N, 24).tolist())), np.int64)
+    ys = yg.t.index_select(0, torch.from_numpy(rows).cuda()).index_select(1, torch.from_numpy(cols).cuda())
+    ys = ys.float().cpu().numpy().astype(np.float64)
+    ref, mag, ref_bf16 = GM.oracle_ref(xq, xs, wq, ws, ends, rows, cols)
+    worst = GM.check(ys, ref, mag, rows, ends, Mx, Kx, True, ref_bf16, what="output past 2^31 elements")
+    print(f"  worst group relative Frobenius error {worst:.3e} over {rows.size} x {cols.size} samples")
