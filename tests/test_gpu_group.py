@@ -225,3 +225,45 @@ def test_hold_and_deferred_routes(route, monkeypatch):
     ends = _sizes_to_ends([1500, 0, 700, 3, 597, 200])   # all 3000 rows in groups
     check_group(x_bits, ends, name=route)
     check_group(x_bits, _sizes_to_ends([1000, 1000]), name=route + " with tail rows")
+
+
+def test_concurrent_calls_on_separate_streams():
+    """The library keeps no state: two group-scaling calls (hold method, row-major;
+    two-pass, column-major) and an MX round trip in flight at once on three
+    streams, each with its own workspace, give the oracle's bytes."""
+    rng = np.random.default_rng(77)
+    xa = (rng.standard_normal((4096, 2048)) * np.exp(rng.standard_normal((4096, 1)))).astype(np.float32)
+    xb = (rng.standard_normal((3000, 1040)) * np.exp(rng.standard_normal((3000, 1)))).astype(np.float32)
+    xa_bits = (xa.view(np.uint32) >> 16).astype(np.uint16)
+    xb_bits = (xb.view(np.uint32) >> 16).astype(np.uint16)
+    ends_a = _sizes_to_ends([1000, 24, 2000, 0, 1072])
+    ends_b = W.zipf_group_ends(3000, 40)
+    xm_bits = W.bf16_bits(W.lognormal_rows(2048, 4096, seed=78).to(torch.bfloat16))
+    xa_d, xb_d, xm_d = U.dev_bf16(xa_bits), U.dev_bf16(xb_bits), U.dev_bf16(xm_bits)
+    oa = torch.from_numpy(ends_a).cuda()
+    ob = torch.from_numpy(ends_b).cuda()
+    qa = torch.empty((4096, 2048), dtype=torch.uint8, device="cuda")
+    sa = torch.empty((len(ends_a), 2048), dtype=torch.float32, device="cuda")
+    qb = torch.empty((1040, 3000), dtype=torch.uint8, device="cuda")
+    sb = torch.empty((len(ends_b), 1040), dtype=torch.float32, device="cuda")
+    wa = torch.empty(mxq.mxq_group_scale_workspace_bytes(4096, 2048, len(ends_a)), dtype=torch.uint8, device="cuda")
+    wb = torch.empty(mxq.mxq_group_scale_workspace_bytes(3000, 1040, len(ends_b)), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    s1, s2, s3 = torch.cuda.Stream(), torch.cuda.Stream(), torch.cuda.Stream()
+    with torch.cuda.stream(s1):
+        mxq.mxq_group_scale_fp8(xa_d, oa, ROW, qa, sa, wa, stream=s1)
+    with torch.cuda.stream(s2):
+        mxq.mxq_group_scale_fp8_ex(xb_d, ob, COL, 0, qb, sb, wb, stream=s2)
+    with torch.cuda.stream(s3):
+        qm, sm = mxq.quantize_mx(xm_d, stream=s3)
+        ym = mxq.dequantize_mx(qm, sm, stream=s3)
+    torch.cuda.synchronize()
+    want_qa, want_sa = oracle.group_scale(xa_bits, ends_a, oracle.LAYOUT_ROW)
+    want_qb, want_sb = oracle.group_scale(xb_bits, ends_b, oracle.LAYOUT_COL)
+    assert np.array_equal(U.host_f32_bits(sa), want_sa.view(np.uint32))
+    assert np.array_equal(U.host_u8(qa), want_qa), U.first_mismatch(U.host_u8(qa), want_qa)
+    assert np.array_equal(U.host_f32_bits(sb), want_sb.view(np.uint32))
+    assert np.array_equal(U.host_u8(qb), want_qb), U.first_mismatch(U.host_u8(qb), want_qb)
+    wq, ws = U.oracle_mx_quantize(xm_bits)
+    assert np.array_equal(U.host_u8(qm), wq) and np.array_equal(U.host_u8(sm), ws)
+    assert np.array_equal(U.host_u16(ym), U.oracle_mx_dequantize(wq, ws))
