@@ -320,7 +320,7 @@ __device__ __forceinline__ void mma_tiles(v16f (&acc)[4][4], const v8i (&a)[4], 
 // k = 16*hk .. +15 and 32 + 16*hk .. +15 (chunks hk and 2 + hk) of its row, and
 // its scale byte covers the 32-k block hk: block 4p + 2Q + hk of the row, which
 // is byte 2Q of the pair's scale word shifted right by 8*hk.
-// MFMA I of the wave's 4 x 4 tiles, then (I < 8) data load I of stage t.
+// MFMA I of the wave's 4 x 4 tiles, then (odd I) data load I/2 of stage t.
 template <int Q, int I>
 __device__ __forceinline__ void mma_step(v16f (&acc)[4][4], const v8i (&a)[4], const v8i (&b)[4], const int (&sa)[4],
                                          const int (&sb)[4], const DataLoads& d, int t)
@@ -328,7 +328,7 @@ __device__ __forceinline__ void mma_step(v16f (&acc)[4][4], const v8i (&a)[4], c
     constexpr int tn = I >> 2, tm = I & 3;
     acc[tn][tm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[tn], b[tm], acc[tn][tm], 0, 0, 2 * Q, sa[tn],
                                                                   2 * Q, sb[tm]);
-    if constexpr (I < 8) issue_data<I>(d, t);
+    if constexpr (I % 2 == 1) issue_data<I / 2>(d, t);
     __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -340,8 +340,9 @@ __device__ __forceinline__ void mma_steps(v16f (&acc)[4][4], const v8i (&a)[4], 
 }
 
 // Stage s = 2p + Q: read its operands from LDS, then issue its 16 MFMAs with
-// the 8 data loads of stage t = s + 3 slotted one after each of the first 8
-// (the loads' issue stalls then overlap the matrix core).
+// the 8 data loads of stage t = s + 3 slotted one after every other MFMA (the
+// loads' issue stalls then overlap the matrix core; measured 2 % faster than
+// one after each of the first 8, and than all 8 before the MFMAs).
 template <int Q>
 __device__ __forceinline__ void mma_stage(v16f (&acc)[4][4], const uint8_t* lds, int s, int wn, int wm, int c32,
                                           int hk, const int (&sa)[4], const int (&sb)[4], const DataLoads& d, int t)
