@@ -207,6 +207,14 @@ size_t mxq_group_scale_workspace_bytes(int64_t M, int64_t K, int32_t G);
  * Requires K % 8 == 0, 0 <= M <= 2^31 - 1024, K <= 2^23, 1 <= G <= 2^20, and
  * the tile count (about (M/128 + G) * K/512) below 2^31 (MXQ_ERR_SHAPE otherwise).
  * K == 0 is a no-op; M == 0 still writes the (G, K) scales.
+ *
+ * Environment, read on each call (the bytes written never depend on it, only
+ * the route and the speed): MXQ_GROUP_MODE=hold|twopass overrides the method
+ * (default: single-read "hold", except two-pass for column-major output with at
+ * least one group per five 128-row blocks); MXQ_GROUP_HOLD_TILES,
+ * MXQ_GROUP_WAIT_US and MXQ_GROUP_STRIP_BLOCK set the hold method's residency
+ * limit, wait bound and launch order, and exist to force its fallback routes
+ * in tests.
  */
 mxq_status mxq_group_scale_fp8(const void* x_bf16, int64_t M, int64_t K,
                                const int32_t* group_end_offs, int32_t G, int out_layout,
