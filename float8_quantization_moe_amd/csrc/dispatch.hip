@@ -12,6 +12,9 @@
 //          writes the cumulative end offsets group_end[e];
 //   place  each pair's rank among the earlier pairs of its block with the same
 //          expert (an LDS scan of the block's 256 ids) gives its row.
+// For small count tables the scan is folded into the place pass (every place
+// workgroup derives its block's first rows from the whole table), which saves
+// the one-workgroup launch.
 // The rows themselves (gather + MX quantize + pack) are written by
 // mx_dispatch_pack_kernel in mx_codec.hip.
 #include "device_common.hpp"
@@ -103,6 +106,67 @@ void dp_place_kernel(const int32_t* __restrict__ ids, int64_t P, int E, const in
     }
 }
 
+// Scan folded into the place pass, for small tables (nblk * E <= kDpFoldMax,
+// E <= kDpThreads): every workgroup reads the whole (blocks x experts) count
+// table from L2 and derives its own block's first row per expert, so the
+// one-workgroup scan launch drops out.  Thread (e, seg) = (tid % E, tid / E)
+// sums expert e's counts over a segment of the blocks: all of them (the
+// expert's total) and those before this block; the totals are then scanned
+// over the experts.  Workgroup 0 also writes the end offsets.
+constexpr int kDpFoldMax = 16384;
+__global__ __launch_bounds__(kDpThreads)
+void dp_place_scan_kernel(const int32_t* __restrict__ ids, int64_t P, int E, int nblk,
+                          const int32_t* __restrict__ bcount, int32_t* __restrict__ src_pair,
+                          int32_t* __restrict__ group_end)
+{
+    __shared__ int tot[kDpThreads], pre[kDpThreads], start[kDpThreads];
+    __shared__ int eid[kDpThreads];
+    const int tid = (int)threadIdx.x;
+    const int b = (int)blockIdx.x;
+    const int S = kDpThreads / E;                        // segments per expert (>= 1)
+    const int e0 = tid % E, seg = tid / E;
+    if (tid < E) {
+        tot[tid] = 0;
+        pre[tid] = 0;
+    }
+    __syncthreads();
+    if (seg < S) {
+        const int len = (nblk + S - 1) / S;
+        const int b0 = seg * len, b1 = b0 + len < nblk ? b0 + len : nblk;
+        int t_sum = 0, p_sum = 0;
+        for (int bb = b0; bb < b1; ++bb) {
+            const int c = bcount[(int64_t)bb * E + e0];
+            t_sum += c;
+            p_sum += bb < b ? c : 0;
+        }
+        atomicAdd(&tot[e0], t_sum);
+        atomicAdd(&pre[e0], p_sum);
+    }
+    __syncthreads();
+    // exclusive scan of the totals over the experts (Hillis-Steele on start[0..E))
+    if (tid < E) start[tid] = tot[tid];
+    __syncthreads();
+    for (int d = 1; d < E; d <<= 1) {
+        int v = 0;
+        if (tid < E && tid >= d) v = start[tid - d];
+        __syncthreads();
+        if (tid < E) start[tid] += v;
+        __syncthreads();
+    }
+    if (b == 0 && tid < E) group_end[tid] = start[tid];  // inclusive: the end of expert tid
+    // the place pass: rank among the earlier pairs of this block with the same expert
+    const int64_t p = (int64_t)b * kDpThreads + tid;
+    int e = p < P ? ids[p] : -1;
+    e = (e >= 0 && e < E) ? e : -1;
+    eid[tid] = e;
+    __syncthreads();
+    if (e >= 0) {
+        int rank = 0;
+        for (int i = 0; i < tid; ++i) rank += eid[i] == e ? 1 : 0;
+        src_pair[start[e] - tot[e] + pre[e] + rank] = (int32_t)p;
+    }
+}
+
 int dispatch_max_experts() { return kDpMaxExperts; }
 
 size_t dispatch_workspace_bytes(int64_t P, int32_t E)
@@ -118,6 +182,11 @@ hipError_t launch_dispatch_order(const int32_t* ids, int64_t P, int E, int32_t* 
     const int nblk = (int)((P + kDpThreads - 1) / kDpThreads);
     if (nblk > 0) {
         hipLaunchKernelGGL(dp_count_kernel, dim3((unsigned)nblk), dim3(kDpThreads), 0, stream, ids, P, E, bcount);
+    }
+    if (nblk > 0 && E <= kDpThreads && (int64_t)nblk * E <= kDpFoldMax) {
+        hipLaunchKernelGGL(dp_place_scan_kernel, dim3((unsigned)nblk), dim3(kDpThreads), 0, stream, ids, P, E, nblk,
+                           (const int32_t*)bcount, src_pair, group_end);
+        return hipGetLastError();
     }
     hipLaunchKernelGGL(dp_scan_kernel, dim3(1), dim3(kDpScanThreads), 0, stream, bcount, nblk, E, group_end);
     if (nblk > 0) {
