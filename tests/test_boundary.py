@@ -236,3 +236,15 @@ def test_product_path_does_not_import_the_oracle():
             if fn.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
                 text = open(os.path.join(dirpath, fn)).read()
                 assert "oracle" not in text.lower(), f"{fn} mentions the oracle"
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """Without the built library every entry point raises: there is no fallback path."""
+    import torch
+    from float8_quantization_moe_amd import mxq
+    monkeypatch.setattr(mxq, "LIB_PATH", str(tmp_path / "libmxq.so"))
+    monkeypatch.setattr(mxq, "_lib", None)
+    with pytest.raises(ImportError, match="libmxq.so not found"):
+        mxq.lib()
+    with pytest.raises(ImportError):
+        mxq.mxq_abi_version()
