@@ -168,6 +168,13 @@ mxq_status mxq_group_scale_fp8_ex(const void* x_bf16, int64_t M, int64_t K, cons
                                               q_e4m3, scales, workspace, (hipStream_t)stream));
 }
 
+mxq_status mxq_set_group_scale_knobs(int method, int hold_tiles, int64_t wait_us, int strip_block)
+{
+    if (method < 0 || method > 2) return MXQ_ERR_RULE;
+    mxq::set_group_scale_knobs(method, hold_tiles, wait_us < 0 ? -1 : (long)wait_us, strip_block);
+    return MXQ_OK;
+}
+
 mxq_status mxq_transpose_u8(const void* in, int64_t R, int64_t C, void* out, void* stream)
 {
     mxq_status st = check_2d(R, C);

@@ -55,10 +55,10 @@
 // consecutive rows per lane, turned into dwords of 4 consecutive rows per
 // column, staged as a 512 x 128-byte transposed tile in LDS, written as 128
 // contiguous bytes per output row.
-#include <stdlib.h>
-#include <string.h>
+#include <atomic>
+#include <mutex>
 
-#include "device_common.hpp"
+#include "group_common.hpp"
 #include "internal.hpp"
 
 namespace mxq {
@@ -158,92 +158,6 @@ size_t group_scale_workspace_bytes(int64_t M, int64_t K, int32_t G)
     return a > b ? a : b;
 }
 
-// ------------------------------------------------------------- helpers ----
-// The multiplier of a column: 448 / max(amax, 1e-12) (correctly rounded divide),
-// or that rounded down to a power of two (clearing the significand: the
-// quotient is always a positive normal, between 448 / bf16 max and 448 / 1e-12).
-__device__ __forceinline__ float group_scale_of(uint32_t amax_bits, int pow2)
-{
-    if (amax_bits >= 0x7F80u) return __uint_as_float(0x7FC00000u);   // Inf/NaN in the column
-    const float amax = __uint_as_float(amax_bits << 16);
-    const float s = 448.0f / fmaxf(amax, 1e-12f);
-    return pow2 ? __uint_as_float(__float_as_uint(s) & 0xFF800000u) : s;
-}
-
-// The stored inverse 1/s of a multiplier (one correctly rounded divide; NaN kept).
-__device__ __forceinline__ float4 inverse4(float4 m)
-{
-    const auto inv = [](float v) { return v != v ? v : 1.0f / v; };
-    return make_float4(inv(m.x), inv(m.y), inv(m.z), inv(m.w));
-}
-
-struct ColScales {
-    float s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    uint32_t nan_lo = 0, nan_hi = 0;   // 0xFF in each byte whose column has a NaN scale
-};
-
-__device__ __forceinline__ ColScales make_col_scales(float4 a, float4 b)
-{
-    ColScales cs;
-    cs.s[0] = a.x; cs.s[1] = a.y; cs.s[2] = a.z; cs.s[3] = a.w;
-    cs.s[4] = b.x; cs.s[5] = b.y; cs.s[6] = b.z; cs.s[7] = b.w;
-    cs.nan_lo = 0;
-    cs.nan_hi = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        if (cs.s[i] != cs.s[i]) cs.nan_lo |= 0xFFu << (8 * i);
-        if (cs.s[i + 4] != cs.s[i + 4]) cs.nan_hi |= 0xFFu << (8 * i);
-    }
-    return cs;
-}
-
-// 8 bf16 of one row (8 consecutive columns) -> 8 E4M3 codes.
-__device__ __forceinline__ uint2 group_quantize_chunk(uint4 v, const ColScales& cs)
-{
-    // binary32 product (one rounding), clamp to +-448, then nearest-even E4M3
-    const float f0 = __builtin_amdgcn_fmed3f(bf16_lo_to_f32(v.x) * cs.s[0], -448.0f, 448.0f);
-    const float f1 = __builtin_amdgcn_fmed3f(bf16_hi_to_f32(v.x) * cs.s[1], -448.0f, 448.0f);
-    const float f2 = __builtin_amdgcn_fmed3f(bf16_lo_to_f32(v.y) * cs.s[2], -448.0f, 448.0f);
-    const float f3 = __builtin_amdgcn_fmed3f(bf16_hi_to_f32(v.y) * cs.s[3], -448.0f, 448.0f);
-    const float f4 = __builtin_amdgcn_fmed3f(bf16_lo_to_f32(v.z) * cs.s[4], -448.0f, 448.0f);
-    const float f5 = __builtin_amdgcn_fmed3f(bf16_hi_to_f32(v.z) * cs.s[5], -448.0f, 448.0f);
-    const float f6 = __builtin_amdgcn_fmed3f(bf16_lo_to_f32(v.w) * cs.s[6], -448.0f, 448.0f);
-    const float f7 = __builtin_amdgcn_fmed3f(bf16_hi_to_f32(v.w) * cs.s[7], -448.0f, 448.0f);
-    int lo = __builtin_amdgcn_cvt_pk_fp8_f32(f0, f1, 0, false);
-    lo = __builtin_amdgcn_cvt_pk_fp8_f32(f2, f3, lo, true);
-    int hi = __builtin_amdgcn_cvt_pk_fp8_f32(f4, f5, 0, false);
-    hi = __builtin_amdgcn_cvt_pk_fp8_f32(f6, f7, hi, true);
-    const uint32_t ulo = ((uint32_t)lo & ~cs.nan_lo) | (0x7F7F7F7Fu & cs.nan_lo);
-    const uint32_t uhi = ((uint32_t)hi & ~cs.nan_hi) | (0x7F7F7F7Fu & cs.nan_hi);
-    return make_uint2(ulo, uhi);
-}
-
-__device__ __forceinline__ void max8(uint4& a, uint4 b)
-{
-    a.x = pk_max_u16(a.x, b.x);
-    a.y = pk_max_u16(a.y, b.y);
-    a.z = pk_max_u16(a.z, b.z);
-    a.w = pk_max_u16(a.w, b.w);
-}
-
-__device__ __forceinline__ uint4 abs8(uint4 v)
-{
-    return make_uint4(v.x & 0x7FFF7FFFu, v.y & 0x7FFF7FFFu, v.z & 0x7FFF7FFFu, v.w & 0x7FFF7FFFu);
-}
-
-// a = max(a, red[1..n-1][cg]), two LDS rows per step so that few registers are
-// live while a tile is held.
-__device__ __forceinline__ void max_rows(uint4& a, const uint4* red, int n, int stride)
-{
-#pragma unroll 1
-    for (int r = 1; r < n; r += 2) {
-        const uint4 b0 = red[r * stride];
-        const uint4 b1 = r + 1 < n ? red[(r + 1) * stride] : make_uint4(0, 0, 0, 0);
-        max8(a, b0);
-        max8(a, b1);
-    }
-}
-
 // Everything a tile needs to know about itself.
 struct TileInfo {
     int g, r0, r1;        // group (G = rows past the last end) and its rows [r0, r1)
@@ -270,63 +184,6 @@ __device__ __forceinline__ TileInfo tile_info(const ChunkEntry* __restrict__ tab
     t.j = j;
     t.s = s;
     return t;
-}
-
-// ---------------------------------------------------- coherent accesses ---
-// Relaxed agent-scope atomics: each access reaches the coherence point shared by
-// all XCDs, so a value written by a workgroup on one XCD is eventually seen by
-// a workgroup polling it on another.
-__device__ __forceinline__ void store_coherent(uint4 v, void* p)
-{
-    unsigned long long* q = (unsigned long long*)p;
-    __hip_atomic_store(q, ((unsigned long long)v.y << 32) | v.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(q + 1, ((unsigned long long)v.w << 32) | v.z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ uint4 load_coherent(const void* p)
-{
-    const unsigned long long* q = (const unsigned long long*)p;
-    const unsigned long long a = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const unsigned long long b = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return make_uint4((uint32_t)a, (uint32_t)(a >> 32), (uint32_t)b, (uint32_t)(b >> 32));
-}
-
-// ------------------------------------------------------ buffer accesses ---
-// Raw buffer accesses through a (base, size) resource: at an offset at or past
-// the size a load reads zero and a store is dropped, without touching memory.
-// X is read once and the codes written once, so both use the streaming
-// (non-temporal) cache policy, which measured about 10 % faster in the hold
-// kernel than the default one.
-typedef __amdgpu_buffer_rsrc_t Rsrc;
-constexpr uint32_t kOOB = 0xFFFFFFF0u;      // above every resource size used here (at most 2^31)
-constexpr int kNonTemporal = 2;             // cache-policy operand of the buffer builtins: nt
-constexpr int kCached = 0;                  // the default policy (lines kept in the caches)
-
-__device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-
-template <int POLICY = kNonTemporal>
-__device__ __forceinline__ uint4 buf_load16(Rsrc r, uint32_t off)
-{
-    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, POLICY);
-    return make_uint4(v.x, v.y, v.z, v.w);
-}
-
-__device__ __forceinline__ void buf_store8(uint2 v, Rsrc r, uint32_t off)
-{
-    const u32x2 w = {v.x, v.y};
-    __builtin_amdgcn_raw_buffer_store_b64(w, r, off, 0, kNonTemporal);
-}
-
-// An opaque copy: the compiler cannot relate the result to its input, so
-// offsets derived from it are recomputed where used instead of being kept in
-// registers from an earlier phase.
-__device__ __forceinline__ int opaque(int v)
-{
-    asm volatile("" : "+v"(v));
-    return v;
 }
 
 // First index i of this lane's rows (C::row(rs, i), increasing in i) at or past
@@ -368,39 +225,6 @@ __device__ __forceinline__ void load_tile(const uint16_t* __restrict__ x, int K,
 #pragma unroll
         for (int i = h * PER; i < (h + 1) * PER; ++i)
             v[i] = buf_load16<POLICY>(r, i >= i0 ? base + (uint32_t)(i - h * PER) * step : kOOB);
-    }
-}
-
-// Byte offset of (column c, row r) inside the column-layout staging tile
-// (256 columns x 128 rows): each column is 128 contiguous bytes whose 16-byte
-// units are XOR-swizzled by bits of the column to spread the LDS banks.
-__device__ __forceinline__ int col_tile_offset(int c, int r)
-{
-    return c * 128 + ((((r >> 4) ^ (c >> 3)) & 7) << 4) + (r & 15);
-}
-
-// Store bytes [lo, hi) of a 16-byte unit at dst (dst 16-byte aligned when
-// `aligned`): the widest naturally aligned pieces that fit, bytes otherwise.
-__device__ __forceinline__ void store_partial16(uint4 val, uint8_t* dst, int lo, int hi, bool aligned)
-{
-    const unsigned long long w[2] = {((unsigned long long)val.y << 32) | val.x,
-                                     ((unsigned long long)val.w << 32) | val.z};
-    int b = lo;
-    while (b < hi) {
-        const unsigned long long word = w[b >> 3] >> (8 * (b & 7));
-        if (aligned && (b & 7) == 0 && hi - b >= 8) {
-            *(unsigned long long*)(dst + b) = word;
-            b += 8;
-        } else if (aligned && (b & 3) == 0 && hi - b >= 4) {
-            *(uint32_t*)(dst + b) = (uint32_t)word;
-            b += 4;
-        } else if (aligned && (b & 1) == 0 && hi - b >= 2) {
-            *(uint16_t*)(dst + b) = (uint16_t)word;
-            b += 2;
-        } else {
-            dst[b] = (uint8_t)word;
-            b += 1;
-        }
     }
 }
 
@@ -575,25 +399,6 @@ void group_plan_kernel(const int32_t* __restrict__ offs, int G, int M, int K, Wo
         e.gr0 = e.gr1 = e.pad = 0;
         ws.table[c] = e;
     }
-}
-
-__device__ __forceinline__ float4 scales_lo(uint4 a, int pow2)
-{
-    return make_float4(group_scale_of(a.x & 0xFFFFu, pow2), group_scale_of(a.x >> 16, pow2),
-                       group_scale_of(a.y & 0xFFFFu, pow2), group_scale_of(a.y >> 16, pow2));
-}
-__device__ __forceinline__ float4 scales_hi(uint4 a, int pow2)
-{
-    return make_float4(group_scale_of(a.z & 0xFFFFu, pow2), group_scale_of(a.z >> 16, pow2),
-                       group_scale_of(a.w & 0xFFFFu, pow2), group_scale_of(a.w >> 16, pow2));
-}
-__device__ __forceinline__ uint4 f4_bits(float4 f)
-{
-    return make_uint4(__float_as_uint(f.x), __float_as_uint(f.y), __float_as_uint(f.z), __float_as_uint(f.w));
-}
-__device__ __forceinline__ float4 bits_f4(uint4 u)
-{
-    return make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w));
 }
 
 // (kPartialUnset has the top bit set, which no |bf16| maximum has.)
@@ -975,19 +780,6 @@ void group_quant_kernel(const uint16_t* __restrict__ x, int M, int K, int G, int
 // group (and loading its 8 scales) whenever a row reaches the group's end.
 // Rows are quantized row-wise (8 codes per row) and the lane's 16 x 8 code
 // block is transposed in registers (byte permutes) into 8 columns of 16 rows.
-__device__ __forceinline__ void transpose4x4_bytes(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3, uint32_t out[4])
-{
-    // w_r holds columns 0..3 of row r; out[c] holds rows 0..3 of column c
-    const uint32_t t01_lo = __builtin_amdgcn_perm(w1, w0, 0x05010400u);   // w0.0 w1.0 w0.1 w1.1
-    const uint32_t t01_hi = __builtin_amdgcn_perm(w1, w0, 0x07030602u);   // w0.2 w1.2 w0.3 w1.3
-    const uint32_t t23_lo = __builtin_amdgcn_perm(w3, w2, 0x05010400u);
-    const uint32_t t23_hi = __builtin_amdgcn_perm(w3, w2, 0x07030602u);
-    out[0] = __builtin_amdgcn_perm(t23_lo, t01_lo, 0x05040100u);
-    out[1] = __builtin_amdgcn_perm(t23_lo, t01_lo, 0x07060302u);
-    out[2] = __builtin_amdgcn_perm(t23_hi, t01_hi, 0x05040100u);
-    out[3] = __builtin_amdgcn_perm(t23_hi, t01_hi, 0x07060302u);
-}
-
 __global__ __launch_bounds__(TileCfg<1>::T)
 void group_quant_col_blocks_kernel(const uint16_t* __restrict__ x, int M, int K, int G, int S, Workspace ws,
                                    const float* __restrict__ scales, uint8_t* __restrict__ q)
@@ -1102,6 +894,55 @@ void group_deferred_kernel(const uint16_t* __restrict__ x, int M, int K, int G, 
 }
 
 // --------------------------------------------------------------- launch ---
+// Route and limit overrides (tests and tuning only; the bytes never depend on
+// them), set process-wide through mxq_set_group_scale_knobs.
+std::atomic<int> g_method{0}, g_hold_tiles{-1}, g_strip_block{0};
+std::atomic<long> g_wait_us{-1};
+
+struct GroupKnobs {
+    int method, hold_tiles, strip_block;
+    long wait_us;
+};
+
+static GroupKnobs group_knobs()
+{
+    return GroupKnobs{g_method.load(std::memory_order_relaxed), g_hold_tiles.load(std::memory_order_relaxed),
+                      g_strip_block.load(std::memory_order_relaxed), g_wait_us.load(std::memory_order_relaxed)};
+}
+
+void set_group_scale_knobs(int method, int hold_tiles, long wait_us, int strip_block)
+{
+    g_method.store(method, std::memory_order_relaxed);
+    g_hold_tiles.store(hold_tiles, std::memory_order_relaxed);
+    g_wait_us.store(wait_us, std::memory_order_relaxed);
+    g_strip_block.store(strip_block, std::memory_order_relaxed);
+}
+
+// Per-device facts the launcher needs, queried once per device.
+struct DeviceInfo {
+    int cus, rate_khz, per_cu[2];
+    bool ok;
+};
+constexpr int kMaxDevices = 64;
+static DeviceInfo g_dev[kMaxDevices];
+static std::once_flag g_dev_once[kMaxDevices];
+
+static const DeviceInfo* device_info()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::call_once(g_dev_once[dev], [dev] {
+        DeviceInfo& d = g_dev[dev];
+        d.ok = hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+               hipDeviceGetAttribute(&d.rate_khz, hipDeviceAttributeWallClockRate, dev) == hipSuccess &&
+               hipOccupancyMaxActiveBlocksPerMultiprocessor(&d.per_cu[0], group_hold_kernel<0>, TileCfg<0>::T, 0) ==
+                   hipSuccess &&
+               hipOccupancyMaxActiveBlocksPerMultiprocessor(&d.per_cu[1], group_hold_kernel<1>, TileCfg<1>::T, 0) ==
+                   hipSuccess;
+    });
+    return g_dev[dev].ok ? &g_dev[dev] : nullptr;
+}
+
 template <int LAYOUT>
 static hipError_t launch_layout(const void* x, int M, int K, const int32_t* offs, int G, int flags, void* q,
                                 float* out_scales, void* workspace, hipStream_t stream)
@@ -1135,36 +976,23 @@ static hipError_t launch_layout(const void* x, int M, int K, const int32_t* offs
     // How many tiles of one group may be held at once: the resident capacity of
     // the hold kernel on this device, less a small margin.  Holding more than
     // fits is still correct (waits time out and the tiles are deferred), only slower.
-    int dev = 0, cus = 0, per_cu = 0, rate_khz = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&rate_khz, hipDeviceAttributeWallClockRate, dev);
-    if (e == hipSuccess)
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, group_hold_kernel<LAYOUT>, C::T, 0);
-    if (e != hipSuccess) return e;
-    // Knobs (read per call): MXQ_GROUP_HOLD_TILES overrides the hold limit (0 sends every
-    // group through the deferred kernel); MXQ_GROUP_WAIT_US bounds each wait (default
-    // 2000 us; 0 makes every waiting tile defer).  Results are identical either way.
-    int hold_limit = cus * per_cu - 16;
-    long wait_us = 2000;
-    int SB = 1;                                           // chunk-fastest launch order (measured best)
-    if (const char* v = getenv("MXQ_GROUP_STRIP_BLOCK")) SB = atoi(v);
-    if (SB < 1 || S % SB != 0) SB = S;
-    if (const char* v = getenv("MXQ_GROUP_HOLD_TILES")) hold_limit = atoi(v);
-    if (const char* v = getenv("MXQ_GROUP_WAIT_US")) wait_us = atol(v);
-    if (wait_us < 0) wait_us = 0;
+    const DeviceInfo* di = device_info();
+    if (!di) return hipErrorInvalidDevice;
+    const GroupKnobs kn = group_knobs();
+    int hold_limit = kn.hold_tiles >= 0 ? kn.hold_tiles : di->cus * di->per_cu[LAYOUT] - 16;
+    const long wait_us = kn.wait_us >= 0 ? kn.wait_us : 2000;
+    int SB = kn.strip_block > 0 ? kn.strip_block : 1;     // chunk-fastest launch order (measured best)
+    if (S % SB != 0) SB = S;
     const unsigned long long timeout_ticks =
-        (unsigned long long)(rate_khz > 0 ? rate_khz : 100000) * (unsigned long long)wait_us / 1000ull;
-    // MXQ_GROUP_MODE=hold|twopass picks the method.  Default: hold, except for
-    // column-major output with more than a few groups, where the hold kernel's
-    // tiles cut at group boundaries split too many output lines (measured at
-    // 16640 x 5120: hold wins at 16 groups, two-pass from 32 on, so the switch is
-    // at about one group per five 128-row blocks).  Row-major output always holds.
+        (unsigned long long)(di->rate_khz > 0 ? di->rate_khz : 100000) * (unsigned long long)wait_us / 1000ull;
+    // The method.  Default: hold, except for column-major output with more than
+    // a few groups, where the hold kernel's tiles cut at group boundaries split
+    // too many output lines (measured at 16640 x 5120: hold wins at 16 groups,
+    // two-pass from 32 on, so the switch is at about one group per five 128-row
+    // blocks).  Row-major output always holds.
     bool twopass = LAYOUT == 1 && 5 * (int64_t)G >= (M + 127) / 128;
-    if (const char* v = getenv("MXQ_GROUP_MODE")) {
-        if (strcmp(v, "twopass") == 0) twopass = true;
-        if (strcmp(v, "hold") == 0) twopass = false;
-    }
+    if (kn.method == 1) twopass = false;
+    if (kn.method == 2) twopass = true;
 
     // the fills are a few MB: give them enough blocks (the scales are polled
     // only by the hold kernel)

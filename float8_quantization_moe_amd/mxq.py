@@ -14,6 +14,7 @@ MoE prototype" (Summary) for the scaled grouped GEMM.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -39,7 +40,10 @@ EXPORTED = ("mxq_abi_version", "mxq_status_string", "mxq_last_hip_error", "mxq_q
             "mxq_dequantize_mx", "mxq_group_scale_workspace_bytes", "mxq_group_scale_fp8",
             "mxq_transpose_u8", "mxq_grouped_mm_workspace_bytes", "mxq_scaled_grouped_mm",
             "mxq_quantize_mx_ex", "mxq_dequantize_mx_ex", "mxq_group_scale_fp8_ex",
-            "mxq_dispatch_pack_workspace_bytes", "mxq_dispatch_pack_mx", "mxq_scaled_grouped_mm_packed")
+            "mxq_dispatch_pack_workspace_bytes", "mxq_dispatch_pack_mx", "mxq_scaled_grouped_mm_packed",
+            "mxq_set_group_scale_knobs")
+
+GROUP_METHODS = {"auto": 0, "hold": 1, "twopass": 2}
 
 
 class MxqError(RuntimeError):
@@ -93,10 +97,29 @@ def lib() -> ctypes.CDLL:
         L.mxq_dispatch_pack_mx.argtypes = [P, i64, i64, P, i32, i32, P, P, P, P, sz, P]
         L.mxq_scaled_grouped_mm_packed.restype = ctypes.c_int
         L.mxq_scaled_grouped_mm_packed.argtypes = [P, P, P, P, i64, i64, i64, i32, ctypes.c_int, P, P, sz, P]
+        L.mxq_set_group_scale_knobs.restype = ctypes.c_int
+        L.mxq_set_group_scale_knobs.argtypes = [ctypes.c_int, ctypes.c_int, i64, ctypes.c_int]
         L.mxq_scaled_grouped_mm.restype = ctypes.c_int
         L.mxq_scaled_grouped_mm.argtypes = [P, P, P, P, P, i64, i64, i64, i32, ctypes.c_int, P, P, sz, P]
         _lib = L
     return _lib
+
+
+def mxq_set_group_scale_knobs(method: str = "auto", hold_tiles: int = -1, wait_us: int = -1,
+                              strip_block: int = 0) -> None:
+    """Test hook: force the group-scaling route (see include/mxq.h).  Defaults restore the automatic choice."""
+    _check(lib().mxq_set_group_scale_knobs(GROUP_METHODS[method], int(hold_tiles), int(wait_us), int(strip_block)),
+           "mxq_set_group_scale_knobs")
+
+
+@contextlib.contextmanager
+def group_scale_knobs(**kw):
+    """Context manager around mxq_set_group_scale_knobs that restores the defaults on exit."""
+    mxq_set_group_scale_knobs(**kw)
+    try:
+        yield
+    finally:
+        mxq_set_group_scale_knobs()
 
 
 def _stream(stream) -> int:

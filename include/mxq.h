@@ -208,13 +208,12 @@ size_t mxq_group_scale_workspace_bytes(int64_t M, int64_t K, int32_t G);
  * the tile count (about (M/128 + G) * K/512) below 2^31 (MXQ_ERR_SHAPE otherwise).
  * K == 0 is a no-op; M == 0 still writes the (G, K) scales.
  *
- * Environment, read on each call (the bytes written never depend on it, only
- * the route and the speed): MXQ_GROUP_MODE=hold|twopass overrides the method
- * (default: single-read "hold", except two-pass for column-major output with at
- * least one group per five 128-row blocks); MXQ_GROUP_HOLD_TILES,
- * MXQ_GROUP_WAIT_US and MXQ_GROUP_STRIP_BLOCK set the hold method's residency
- * limit, wait bound and launch order, and exist to force its fallback routes
- * in tests.
+ * Two methods, picked on the host from the sizes alone: "hold" (X read once,
+ * tiles held on chip until their group's scales are known) for row-major
+ * output and for column-major output with fewer than one group per five
+ * 128-row blocks, "two-pass" (an amax pass, then a quantize pass that reads X
+ * again) otherwise.  Both give the same bytes; mxq_set_group_scale_knobs can
+ * force either one.
  */
 mxq_status mxq_group_scale_fp8(const void* x_bf16, int64_t M, int64_t K,
                                const int32_t* group_end_offs, int32_t G, int out_layout,
@@ -242,6 +241,27 @@ mxq_status mxq_group_scale_fp8_ex(const void* x_bf16, int64_t M, int64_t K,
                                   const int32_t* group_end_offs, int32_t G, int out_layout, int flags,
                                   void* q_e4m3, float* scales,
                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Test and tuning hook, not for production code: overrides how
+ * mxq_group_scale_fp8 / mxq_group_scale_fp8_ex route their work, for every
+ * later call in the process (the bytes written never depend on it, only the
+ * route and the speed).
+ *   method       0 = automatic (the default), 1 = hold, 2 = two-pass.
+ *   hold_tiles   the hold method's limit on tiles of one group held on chip at
+ *                once (larger groups go through its deferred pass); < 0 = the
+ *                device's resident capacity less 16 (the default); 0 defers
+ *                every group.
+ *   wait_us      bound on each of the hold method's waits, in microseconds;
+ *                < 0 = 2000 (the default); 0 makes every waiting tile take its
+ *                fallback at once.
+ *   strip_block  the hold method's launch order (strips per block of
+ *                consecutive workgroups); <= 0 = 1 (the default).
+ * MXQ_ERR_RULE for a method outside 0..2.  It is a process-wide setting that
+ * concurrent calls read without synchronisation: change it only while no
+ * group-scaling call is being issued.
+ */
+mxq_status mxq_set_group_scale_knobs(int method, int hold_tiles, int64_t wait_us, int strip_block);
 
 /*
  * Byte transpose: out (C, R) = in (R, C)^T, both row-major.  The layout

@@ -14,3 +14,12 @@ if HERE not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: takes more than a few seconds on the CPU")
+
+
+@pytest.fixture
+def group_knobs():
+    """Force the group-scaling route for one test (mxq_set_group_scale_knobs);
+    the automatic choice is restored afterwards."""
+    from float8_quantization_moe_amd import mxq
+    yield mxq.mxq_set_group_scale_knobs
+    mxq.mxq_set_group_scale_knobs()

@@ -127,6 +127,9 @@ def test_group_scale_argument_errors(L):
     assert f(A, 512, 0, A, 4, 0, A, A, A, ws, S) == 0             # K == 0: no-op
     fx = L.mxq_group_scale_fp8_ex
     assert fx(A, 512, 256, A, 4, 0, 4, A, A, A, ws, S) == 9      # unknown flag bit
+    k = L.mxq_set_group_scale_knobs                              # the route hook: method 0..2 only
+    assert k(3, -1, -1, 0) == 9 and k(-1, -1, -1, 0) == 9
+    assert k(2, 5, 0, 2) == 0 and k(0, -1, -1, 0) == 0
     assert fx(A, 512, 256, A, 4, 0, -1, A, A, A, ws, S) == 9
     assert fx(A, 512, 256, A, 4, 2, 1, A, A, A, ws, S) == 4      # layout before flags
     assert fx(A, 512, 252, A, 4, 0, 3, A, A, A, ws, S) == 2

@@ -95,8 +95,8 @@ MODES = ["hold", "twopass"]
 
 @pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("case", list(EDGE_CASES), ids=list(EDGE_CASES))
-def test_edge_cases(case, mode, monkeypatch):
-    monkeypatch.setenv("MXQ_GROUP_MODE", mode)
+def test_edge_cases(case, mode, group_knobs):
+    group_knobs(method=mode)
     M, K, sizes = EDGE_CASES[case]
     rng = np.random.default_rng(len(case) * 1000 + M)
     if sizes is None:
@@ -109,8 +109,8 @@ def test_edge_cases(case, mode, monkeypatch):
 
 
 @pytest.mark.parametrize("mode", MODES)
-def test_out_of_contract_offsets_are_clamped(mode, monkeypatch):
-    monkeypatch.setenv("MXQ_GROUP_MODE", mode)
+def test_out_of_contract_offsets_are_clamped(mode, group_knobs):
+    group_knobs(method=mode)
     M, K = 300, 64
     rng = np.random.default_rng(21)
     x_bits = (rng.standard_normal((M, K)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
@@ -119,8 +119,8 @@ def test_out_of_contract_offsets_are_clamped(mode, monkeypatch):
 
 
 @pytest.mark.parametrize("mode", MODES)
-def test_nonfinite_columns(mode, monkeypatch):
-    monkeypatch.setenv("MXQ_GROUP_MODE", mode)
+def test_nonfinite_columns(mode, group_knobs):
+    group_knobs(method=mode)
     M, K = 260, 48
     rng = np.random.default_rng(22)
     x_bits = (rng.standard_normal((M, K)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
@@ -149,9 +149,9 @@ def tokens_bits():
 
 
 @pytest.mark.parametrize("mode", MODES)
-def test_tokens_g16_full_size(tokens_bits, mode, monkeypatch):
+def test_tokens_g16_full_size(tokens_bits, mode, group_knobs):
     """(16640, 5120), 16 Zipf(1.1) groups, both layouts, both methods: every byte."""
-    monkeypatch.setenv("MXQ_GROUP_MODE", mode)
+    group_knobs(method=mode)
     ends = W.zipf_group_ends(W.TOKENS_SHAPE[0], 16)
     check_group(tokens_bits, ends, name=f"G=16 {mode}")
 
@@ -194,29 +194,25 @@ def test_transpose_shapes(R, C):
 
 # The hold method keeps each tile on chip until its group's scales are known;
 # groups too large to hold, and tiles whose bounded wait runs out, go through
-# the deferred kernel.  The two-pass method's last arrivals poll partial rows
-# (bounded too).  Force every route from the host and check the bytes.
-HOLD = {"MXQ_GROUP_MODE": "hold"}
+# the deferred kernel, or (when no deferred pass is launched) reduce their
+# strip from the input.  Force every route from the host and check the bytes.
 ROUTES = {
-    "held": {**HOLD},
-    "all_streamed": {**HOLD, "MXQ_GROUP_HOLD_TILES": "0"},
+    "held": dict(method="hold"),
+    "all_streamed": dict(method="hold", hold_tiles=0),
     # no deferred pass is launched for these sizes: timed-out tiles finish themselves
-    "all_waits_time_out": {**HOLD, "MXQ_GROUP_WAIT_US": "0"},
+    "all_waits_time_out": dict(method="hold", wait_us=0),
     # groups of more than 5 chunks streamed, smaller ones held
-    "small_hold_limit": {**HOLD, "MXQ_GROUP_HOLD_TILES": "5"},
+    "small_hold_limit": dict(method="hold", hold_tiles=5),
     # deferred pass launched and every waiting tile defers to it
-    "time_outs_deferred": {**HOLD, "MXQ_GROUP_HOLD_TILES": "5", "MXQ_GROUP_WAIT_US": "0"},
-    "launch_order_strip_fastest": {**HOLD, "MXQ_GROUP_STRIP_BLOCK": "2"},
-    "twopass": {"MXQ_GROUP_MODE": "twopass"},
-    # a partial row not yet visible to the last arrival: reduce from the input
-    "twopass_waits_time_out": {"MXQ_GROUP_MODE": "twopass", "MXQ_GROUP_WAIT_US": "0"},
+    "time_outs_deferred": dict(method="hold", hold_tiles=5, wait_us=0),
+    "launch_order_strip_fastest": dict(method="hold", strip_block=2),
+    "twopass": dict(method="twopass"),
 }
 
 
 @pytest.mark.parametrize("route", list(ROUTES), ids=list(ROUTES))
-def test_hold_and_deferred_routes(route, monkeypatch):
-    for k, v in ROUTES[route].items():
-        monkeypatch.setenv(k, v)
+def test_hold_and_deferred_routes(route, group_knobs):
+    group_knobs(**ROUTES[route])
     M, K = 3000, 1040
     rng = np.random.default_rng(31)
     x = (rng.standard_normal((M, K)) * np.exp(rng.standard_normal((M, 1)))).astype(np.float32)

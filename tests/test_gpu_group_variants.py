@@ -98,8 +98,8 @@ EDGE = {
 @pytest.mark.parametrize("mode", ["hold", "twopass"])
 @pytest.mark.parametrize("flags", FLAGS, ids=FIDS)
 @pytest.mark.parametrize("case", list(EDGE), ids=list(EDGE))
-def test_edge_cases(case, flags, mode, monkeypatch):
-    monkeypatch.setenv("MXQ_GROUP_MODE", mode)
+def test_edge_cases(case, flags, mode, group_knobs):
+    group_knobs(method=mode)
     M, K, sizes = EDGE[case]
     rng = np.random.default_rng(M + K)
     x_bits = _bits(rng, M, K)
@@ -109,18 +109,17 @@ def test_edge_cases(case, flags, mode, monkeypatch):
 
 
 ROUTES = {
-    "held": {"MXQ_GROUP_MODE": "hold"},
-    "all_streamed": {"MXQ_GROUP_MODE": "hold", "MXQ_GROUP_HOLD_TILES": "0"},
-    "time_outs_deferred": {"MXQ_GROUP_MODE": "hold", "MXQ_GROUP_HOLD_TILES": "5", "MXQ_GROUP_WAIT_US": "0"},
-    "all_waits_time_out": {"MXQ_GROUP_MODE": "hold", "MXQ_GROUP_WAIT_US": "0"},
+    "held": dict(method="hold"),
+    "all_streamed": dict(method="hold", hold_tiles=0),
+    "time_outs_deferred": dict(method="hold", hold_tiles=5, wait_us=0),
+    "all_waits_time_out": dict(method="hold", wait_us=0),
 }
 
 
 @pytest.mark.parametrize("route", list(ROUTES), ids=list(ROUTES))
-def test_routes_pow2_inverse(route, monkeypatch):
+def test_routes_pow2_inverse(route, group_knobs):
     """Every route of the hold method writes the multipliers it uses and the stored 1/s."""
-    for k, v in ROUTES[route].items():
-        monkeypatch.setenv(k, v)
+    group_knobs(**ROUTES[route])
     rng = np.random.default_rng(41)
     x_bits = _bits(rng, 3000, 1040)
     check_variant(x_bits, np.cumsum([1500, 0, 700, 3, 597, 200]).astype(np.int32), POW2 | INV, name=route)

@@ -93,11 +93,11 @@ def test_mx_dim0_past_2_31_elements(x):
 
 
 @pytest.mark.parametrize("mode", ["hold", "twopass"])
-def test_group_scaling_and_transform_past_2_31_elements(x, mode, monkeypatch):
+def test_group_scaling_and_transform_past_2_31_elements(x, mode, group_knobs):
     """16 Zipf groups (the largest far beyond what one launch can hold, so the
     hold method streams it through its deferred pass), row-major and
     column-major, and the transform of the column-major codes."""
-    monkeypatch.setenv("MXQ_GROUP_MODE", mode)
+    group_knobs(method=mode)
     G = 16
     ends = W.zipf_group_ends(M, G)
     print(f"group scaling M={M} K={K} G={G} mode={mode}", flush=True)

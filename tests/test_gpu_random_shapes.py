@@ -90,8 +90,8 @@ def test_mx_dim0_random(seed):
 
 @pytest.mark.parametrize("mode", ["hold", "twopass"])
 @pytest.mark.parametrize("seed", range(8))
-def test_group_scaling_random(seed, mode, monkeypatch):
-    monkeypatch.setenv("MXQ_GROUP_MODE", mode)
+def test_group_scaling_random(seed, mode, group_knobs):
+    group_knobs(method=mode)
     rng = np.random.default_rng(3000 + seed)
     M = int(rng.integers(1, 5000))
     K = 8 * int(rng.integers(1, 300))
