@@ -168,6 +168,27 @@ mxq_status mxq_group_scale_fp8_ex(const void* x_bf16, int64_t M, int64_t K, cons
                                               q_e4m3, scales, workspace, (hipStream_t)stream));
 }
 
+mxq_status mxq_group_scale_fp8_noalloc(const void* x_bf16, int64_t M, int64_t K, const int32_t* group_end_offs,
+                                       int32_t G, int out_layout, int flags, void* q_e4m3, float* scales,
+                                       void* stream)
+{
+    mxq_status st = check_group_sizes(M, K, G);
+    if (st != MXQ_OK) return st;
+    if (out_layout != MXQ_LAYOUT_ROW && out_layout != MXQ_LAYOUT_COL) return MXQ_ERR_LAYOUT;
+    if ((flags & ~(MXQ_GROUP_POW2_SCALE | MXQ_GROUP_INVERSE_SCALE)) != 0) return MXQ_ERR_RULE;
+    if (K == 0) return MXQ_OK;
+    if (!group_end_offs || !scales) return MXQ_ERR_NULL;
+    if (M > 0 && (!x_bf16 || !q_e4m3)) return MXQ_ERR_NULL;
+    if (!aligned16(scales) || (M > 0 && (!aligned16(x_bf16) || !aligned16(q_e4m3)))) return MXQ_ERR_ALIGN;
+    if (((uintptr_t)group_end_offs & 3u) != 0) return MXQ_ERR_ALIGN;
+    if (mxq::group_scale_workspace_bytes(M, K, G) > mxq::kNoAllocScratchBytes) return MXQ_ERR_WORKSPACE;
+    void* ws = nullptr;
+    const hipError_t e = mxq::group_scale_scratch(&ws);
+    if (e != hipSuccess) return hip_status(e);
+    return hip_status(mxq::launch_group_scale(x_bf16, (int)M, (int)K, group_end_offs, (int)G, out_layout, flags,
+                                              q_e4m3, scales, ws, (hipStream_t)stream));
+}
+
 mxq_status mxq_set_group_scale_knobs(int method, int hold_tiles, int64_t wait_us, int strip_block)
 {
     if (method < 0 || method > 2) return MXQ_ERR_RULE;

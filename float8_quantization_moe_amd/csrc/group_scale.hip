@@ -1033,6 +1033,35 @@ static hipError_t launch_layout(const void* x, int M, int K, const int32_t* offs
     return hipGetLastError();
 }
 
+// ----------------------------------------------------- allocation-free ---
+// Scratch for callers that cannot allocate (code under graph capture, serving
+// loops, harnesses that forbid hipMalloc): one array per device, alive until
+// the process ends.  In host code `scratch` only names the symbol; its device
+// address is looked up once per device (with that device current) and used
+// everywhere instead.  Every call on a device shares its array, so calls that
+// overlap on one device race.  Nothing in it needs to survive a call: the
+// plan kernel re-initialises all that the other kernels read.
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+static void* g_scratch_ptr[kMaxDevices];
+static hipError_t g_scratch_err[kMaxDevices];
+static std::once_flag g_scratch_once[kMaxDevices];
+
+hipError_t group_scale_scratch(void** ptr)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::call_once(g_scratch_once[dev], [dev] {
+        void* p = nullptr;
+        g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        g_scratch_ptr[dev] = p;
+    });
+    if (g_scratch_err[dev] != hipSuccess) return g_scratch_err[dev];
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
 hipError_t launch_group_scale(const void* x, int M, int K, const int32_t* offs, int G, int layout, int flags,
                               void* q, float* scales, void* workspace, hipStream_t stream)
 {

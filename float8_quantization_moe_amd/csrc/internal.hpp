@@ -26,6 +26,10 @@ size_t group_scale_workspace_bytes(int64_t M, int64_t K, int32_t G);
 // Route overrides for tests (process-wide): method 0 auto, 1 hold, 2 two-pass;
 // hold_tiles < 0, wait_us < 0 and strip_block <= 0 select the defaults.
 void set_group_scale_knobs(int method, int hold_tiles, long wait_us, int strip_block);
+// The allocation-free variant's scratch: a static device array of this many
+// bytes per device, its address on the current device.
+constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
+hipError_t group_scale_scratch(void** ptr);
 hipError_t launch_group_scale(const void* x, int M, int K, const int32_t* offs, int G, int layout, int flags,
                               void* q, float* scales, void* workspace, hipStream_t stream);
 

@@ -41,7 +41,7 @@ EXPORTED = ("mxq_abi_version", "mxq_status_string", "mxq_last_hip_error", "mxq_q
             "mxq_transpose_u8", "mxq_grouped_mm_workspace_bytes", "mxq_scaled_grouped_mm",
             "mxq_quantize_mx_ex", "mxq_dequantize_mx_ex", "mxq_group_scale_fp8_ex",
             "mxq_dispatch_pack_workspace_bytes", "mxq_dispatch_pack_mx", "mxq_scaled_grouped_mm_packed",
-            "mxq_set_group_scale_knobs")
+            "mxq_set_group_scale_knobs", "mxq_group_scale_fp8_noalloc")
 
 GROUP_METHODS = {"auto": 0, "hold": 1, "twopass": 2}
 
@@ -97,6 +97,8 @@ def lib() -> ctypes.CDLL:
         L.mxq_dispatch_pack_mx.argtypes = [P, i64, i64, P, i32, i32, P, P, P, P, sz, P]
         L.mxq_scaled_grouped_mm_packed.restype = ctypes.c_int
         L.mxq_scaled_grouped_mm_packed.argtypes = [P, P, P, P, i64, i64, i64, i32, ctypes.c_int, P, P, sz, P]
+        L.mxq_group_scale_fp8_noalloc.restype = ctypes.c_int
+        L.mxq_group_scale_fp8_noalloc.argtypes = [P, i64, i64, P, i32, ctypes.c_int, ctypes.c_int, P, P, P]
         L.mxq_set_group_scale_knobs.restype = ctypes.c_int
         L.mxq_set_group_scale_knobs.argtypes = [ctypes.c_int, ctypes.c_int, i64, ctypes.c_int]
         L.mxq_scaled_grouped_mm.restype = ctypes.c_int
@@ -246,6 +248,21 @@ def mxq_group_scale_fp8_ex(x: torch.Tensor, group_end_offs: torch.Tensor, out_la
     wbytes = workspace.numel() * workspace.element_size()
     _check(lib().mxq_group_scale_fp8_ex(px, M, K, po, G, int(out_layout), int(flags), pq, ps, pw, wbytes,
                                         _stream(stream)), "mxq_group_scale_fp8_ex")
+
+
+def mxq_group_scale_fp8_noalloc(x: torch.Tensor, group_end_offs: torch.Tensor, out_layout: int, flags: int,
+                                q: torch.Tensor, scales: torch.Tensor, stream=None) -> None:
+    """mxq_group_scale_fp8_ex with the library's static per-GPU scratch instead of a workspace."""
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D (M, K)")
+    M, K = x.shape
+    G = group_end_offs.numel()
+    px = _dev(x, "x", torch.bfloat16)
+    po = _dev(group_end_offs, "group_end_offs", torch.int32)
+    pq = _dev(q, "q", torch.uint8, M * K)
+    ps = _dev(scales, "scales", torch.float32, G * K)
+    _check(lib().mxq_group_scale_fp8_noalloc(px, M, K, po, G, int(out_layout), int(flags), pq, ps,
+                                             _stream(stream)), "mxq_group_scale_fp8_noalloc")
 
 
 def mxq_transpose_u8(inp: torch.Tensor, out: torch.Tensor, stream=None) -> None:

@@ -243,6 +243,25 @@ mxq_status mxq_group_scale_fp8_ex(const void* x_bf16, int64_t M, int64_t K,
                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * mxq_group_scale_fp8_ex without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  It allocates nothing and calls no
+ * allocating routine: its scratch is a static device array of 16 MiB per GPU
+ * that the library holds until the process ends (the address is looked up
+ * once per device, on the first call there).
+ *   Arguments, results, flags and errors as mxq_group_scale_fp8_ex, plus
+ *   MXQ_ERR_WORKSPACE when mxq_group_scale_workspace_bytes(M, K, G) exceeds
+ *   16 MiB (checked on the host before anything is enqueued; for example
+ *   (16640, 5120) needs at most 5.3 MB at 128 groups).
+ * Every call on one GPU uses that GPU's single array: calls that overlap on
+ * one GPU (different streams, or several host threads) race and must not be
+ * issued; calls in stream order on one stream are fine.
+ */
+mxq_status mxq_group_scale_fp8_noalloc(const void* x_bf16, int64_t M, int64_t K,
+                                       const int32_t* group_end_offs, int32_t G, int out_layout,
+                                       int flags, void* q_e4m3, float* scales, void* stream);
+
+/*
  * Test and tuning hook, not for production code: overrides how
  * mxq_group_scale_fp8 / mxq_group_scale_fp8_ex route their work, for every
  * later call in the process (the bytes written never depend on it, only the

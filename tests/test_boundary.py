@@ -127,6 +127,15 @@ def test_group_scale_argument_errors(L):
     assert f(A, 512, 0, A, 4, 0, A, A, A, ws, S) == 0             # K == 0: no-op
     fx = L.mxq_group_scale_fp8_ex
     assert fx(A, 512, 256, A, 4, 0, 4, A, A, A, ws, S) == 9      # unknown flag bit
+    na = L.mxq_group_scale_fp8_noalloc                           # allocation-free variant: host checks first
+    assert na(A, 512, 252, A, 4, 0, 0, A, A, S) == 2              # K % 8
+    assert na(A, 512, 256, A, 4, 2, 0, A, A, S) == 4              # layout
+    assert na(A, 512, 256, A, 4, 0, 4, A, A, S) == 9              # flag
+    assert na(A, 512, 256, A, 4, 0, 0, 0, A, S) == 1              # null q
+    assert na(A, 512, 256, A + 2, 4, 0, 0, A, A, S) == 3          # misaligned offsets
+    assert L.mxq_group_scale_workspace_bytes(262144, 8192, 16) > (16 << 20)
+    assert na(A, 262144, 8192, A, 16, 0, 0, A, A, S) == 5         # needs more than the 16 MiB scratch
+    assert na(A, 512, 0, A, 4, 0, 0, A, A, S) == 0                # K == 0: no-op
     k = L.mxq_set_group_scale_knobs                              # the route hook: method 0..2 only
     assert k(3, -1, -1, 0) == 9 and k(-1, -1, -1, 0) == 9
     assert k(2, 5, 0, 2) == 0 and k(0, -1, -1, 0) == 0
