@@ -16,7 +16,9 @@ and "[moe training] fix uncoalesced global accesses in per group rowwise scaling
 kernel" (Summary; Performance tables at (16640, 5120), 16..128 groups).
 
 The metric is achieved HBM bandwidth: algorithmic bytes (each input read once,
-each output written once) over time.  Inputs are resident in device memory
+each output written once) over time.  The step's bytes are those of the method:
+the transform in call 5 is overhead (it moves 2 more bytes per element), so it
+is timed inside the step but its bytes are reported apart, not counted.  Inputs are resident in device memory
 before timing starts; several independent buffer sets are rotated so that no
 step finds the previous step's data in the 256 MB last-level cache.
 
@@ -157,8 +159,8 @@ def ingest_counters(stats_csv, fetch_csv, write_csv, sq_csv=None, commands=""):
              ("group scaling G=128 column-major (plan + amax + finalize + quantize)",
               ["mxq::group_plan_kernel<128>", "mxq::group_amax_kernel<1>", "mxq::group_finalize_kernel",
                "mxq::group_quant_col_blocks_kernel"], group_bytes(TOKENS[0], TOKENS[1], 128)),
-             ("dispatch pack, top-1 over 16 experts (count + scan + place + pack)",
-              ["mxq::dp_count_kernel", "mxq::dp_scan_kernel", "mxq::dp_place_kernel", "mxq::mx_dispatch_pack_kernel"],
+             ("dispatch pack, top-1 over 16 experts (count + place with the scan folded in + pack)",
+              ["mxq::dp_count_kernel", "mxq::dp_place_scan_kernel", "mxq::mx_dispatch_pack_kernel"],
               mx_bytes(*DISPATCH) + 8 * DISPATCH[0])]
     lines += ["", "Whole calls (sum of the kernels each call launches):", "",
               "| call | scaled HBM bytes | algorithmic bytes | ratio |", "|---|---|---|---|"]
@@ -190,6 +192,47 @@ def ingest_counters(stats_csv, fetch_csv, write_csv, sq_csv=None, commands=""):
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(out, f, indent=1)
     print("\n".join(lines))
+
+
+def launch_stats(torch, stream, fn, reps):
+    """Per-launch durations (us) of fn(i), i = 0..reps-1, each bracketed by its own
+    events on `stream`: mean, median, min and p90."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for i in range(reps):
+        evs[i][0].record(stream)
+        fn(i)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    t = sorted(e[0].elapsed_time(e[1]) * 1e3 for e in evs)
+    return {"avg_us": round(sum(t) / len(t), 2), "median_us": round(t[len(t) // 2], 2), "min_us": round(t[0], 2),
+            "p90_us": round(t[min(len(t) - 1, int(0.9 * len(t)))], 2)}
+
+
+def rate(nbytes, us):
+    return {"algorithmic_bytes": nbytes, "GBps": round(nbytes / (us * 1e3), 1),
+            "frac_of_peak": round(nbytes / (us * 1e3) / HBM_PEAK_GBPS, 4)}
+
+
+def device_facts(torch):
+    """Name, CUs, L2, clocks and memory bus of device 0, from torch's properties and
+    hipDeviceGetAttribute of the HIP runtime torch has loaded (attribute numbers of
+    hip_runtime_api.h's hipDeviceAttribute_t; checked against the CU count)."""
+    import ctypes
+    props = torch.cuda.get_device_properties(0)
+    out = {"name": props.name, "arch": getattr(props, "gcnArchName", ""), "cus": props.multi_processor_count,
+           "l2_bytes_per_xcd": getattr(props, "L2_cache_size", None), "hbm_bytes": props.total_memory}
+    try:
+        path = next(l.split()[-1] for l in open("/proc/self/maps") if "libamdhip64.so" in l)
+        hip = ctypes.CDLL(path)
+        def attr(a):
+            v = ctypes.c_int(0)
+            return v.value if hip.hipDeviceGetAttribute(ctypes.byref(v), a, 0) == 0 else None
+        if attr(63) == props.multi_processor_count:          # hipDeviceAttributeMultiprocessorCount
+            out.update({"peak_sclk_mhz": attr(5) / 1000, "peak_mclk_mhz": attr(60) / 1000,
+                        "memory_bus_bits": attr(59), "l2_bytes_per_xcd": attr(19)})
+    except (StopIteration, OSError, TypeError):
+        pass
+    return out
 
 
 def cpu_info():
@@ -368,7 +411,9 @@ def main():
         "group_scale_g128_col": group_bytes(M2, K2, G_COL),
         "transpose_col_to_row": transpose_bytes(M2, K2),
     }
-    step_bytes = sum(call_bytes.values())
+    # the method's bytes: the transform (call 5) is overhead, timed but not counted
+    step_bytes = sum(v for c, v in call_bytes.items() if c != "transpose_col_to_row")
+    transform_bytes = call_bytes["transpose_col_to_row"]
     stream = torch.cuda.current_stream()
 
     def call_fns(b):
@@ -408,6 +453,8 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         per_call_us[c] = e0.elapsed_time(e1) * 1e3 / reps
+    per_call_dist = {c: launch_stats(torch, stream, lambda r, j=j: fns_per_set[r % len(sets)][j](), reps)
+                     for j, c in enumerate(calls)}
     # Variants of the path's calls (the NEXT rows), each alone on the same rotated
     # buffers and shapes; reported beside the step, not part of `value`.
     FLOOR, RCEIL = mxq.MXQ_SCALE_FLOOR, mxq.MXQ_SCALE_RCEIL
@@ -483,6 +530,63 @@ def main():
                                                 "frac_of_peak": round(nb / (us * 1e3) / HBM_PEAK_GBPS, 4),
                                                 "shape": [M2, WGRAD_N]}
     del dy, qdy, sdy, wsdy
+    # ---------------------------------------------- (16640, 5120) sweeps ---
+    # Per-group scaling over the pages' sweep (16 to 128 groups) in both layouts,
+    # and the column-major route followed by the transform back, timed as one
+    # unit (its bytes: the method's; the transform's are overhead).  Each call
+    # bracketed by its own events; medians reported.
+    group_sweep = {}
+    qsets = [torch.empty((M2, K2), dtype=torch.uint8, device=dev) for _ in range(2)]
+    qt = torch.empty((M2, K2), dtype=torch.uint8, device=dev)
+    for G in (16, 32, 64, 128):
+        offs = torch.from_numpy(W.zipf_group_ends(M2, G, seed=1)).to(dev)
+        sc = torch.empty((G, K2), dtype=torch.float32, device=dev)
+        wsg = torch.empty(mxq.mxq_group_scale_workspace_bytes(M2, K2, G), dtype=torch.uint8, device=dev)
+        nb = group_bytes(M2, K2, G)
+        fns = {
+            "row": lambda i: mxq.mxq_group_scale_fp8(sets[i % len(sets)].x2, offs, ROW, qsets[i % 2], sc, wsg, stream),
+            "col": lambda i: mxq.mxq_group_scale_fp8(sets[i % len(sets)].x2, offs, COL, qsets[i % 2], sc, wsg, stream),
+            "col_then_transform_to_row": lambda i: (
+                mxq.mxq_group_scale_fp8(sets[i % len(sets)].x2, offs, COL, qsets[i % 2], sc, wsg, stream),
+                mxq.mxq_transpose_u8(qsets[i % 2].view(K2, M2), qt, stream)),
+        }
+        for name, fn in fns.items():
+            for i in range(2):
+                fn(i)
+            st = launch_stats(torch, stream, fn, reps)
+            group_sweep[f"g{G}_{name}"] = {**st, **rate(nb, st["median_us"])}
+        del offs, sc, wsg
+    del qsets, qt
+    # MX quantize / dequantize at the token shape (the target names both shapes)
+    xq_t = torch.empty((M2, K2), dtype=torch.uint8, device=dev)
+    xs_t = torch.empty((M2, K2 // 32), dtype=torch.uint8, device=dev)
+    y_t = torch.empty((M2, K2), dtype=torch.bfloat16, device=dev)
+    mx_tokens = {}
+    for name, fn in (("mx_quantize", lambda i: mxq.mxq_quantize_mx(sets[i % len(sets)].x2, xq_t, xs_t, stream)),
+                     ("mx_dequantize", lambda i: mxq.mxq_dequantize_mx(xq_t, xs_t, y_t, stream))):
+        for i in range(2):
+            fn(i)
+        st = launch_stats(torch, stream, fn, reps)
+        mx_tokens[name] = {**st, **rate(mx_bytes(M2, K2), st["median_us"]), "shape": [M2, K2]}
+    del xq_t, xs_t, y_t
+    # Group scaling (16 groups, row-major: the hold method, which keeps a group's
+    # tiles resident together) while a streaming copy of 2 GiB runs on a second
+    # stream of the same GPU, against the same call alone.
+    side = torch.cuda.Stream()
+    big_src = torch.empty(1 << 31, dtype=torch.uint8, device=dev)
+    big_dst = torch.empty_like(big_src)
+    g16 = lambda i: mxq.mxq_group_scale_fp8(sets[i % len(sets)].x2, offs16, ROW, sets[0].q2, sets[0].sc2, ws, stream)
+    alone = launch_stats(torch, stream, g16, 10)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        for _ in range(4):
+            big_dst.copy_(big_src)                        # about 4 x 0.8 ms of copying queued on the side stream
+    beside = launch_stats(torch, stream, g16, 10)         # issued at once, overlapping the copies
+    torch.cuda.synchronize()
+    concurrency = {"what": ("group scaling (16640, 5120), 16 groups, row-major, while 2 GiB device copies run "
+                            "on a second stream; per-launch events on the call's stream"),
+                   "alone": alone, "beside_streaming_copy": beside}
+    del big_src, big_dst, side
     for i in range(2):
         step(i)
     torch.cuda.synchronize()
@@ -507,10 +611,9 @@ def main():
     dev_ms = t_start.elapsed_time(t_end) / args.steps
     ms_per_step = max(host_ms, dev_ms)
     dom_us = 1e3 * float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    kernels = {c: {"avg_us": round(per_call_us[c], 2), "algorithmic_bytes": call_bytes[c],
-                   "GBps": round(call_bytes[c] / (per_call_us[c] * 1e3), 1),
-                   "frac_of_peak": round(call_bytes[c] / (per_call_us[c] * 1e3) / HBM_PEAK_GBPS, 4)}
-               for c in calls}
+    kernels = {c: {"avg_us": round(per_call_us[c], 2), **rate(call_bytes[c], per_call_us[c]),
+                   "per_launch": per_call_dist[c]} for c in calls}
+    kernels["transpose_col_to_row"]["note"] = "overhead of the column-major route: not in step_algorithmic_bytes"
     value = step_bytes / (ms_per_step * 1e6)          # GB/s
 
     # streaming ceiling for context: a device-to-device copy of 1 GiB
@@ -613,7 +716,6 @@ def main():
                           "split": "MX rows, group-scaling columns, statically over the threads"},
         }
 
-    props = torch.cuda.get_device_properties(0)
     out = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -634,16 +736,20 @@ def main():
             "dispatch_shape": list(DISPATCH), "tokens_shape": list(TOKENS),
             "groups_row": G_ROW, "groups_col": G_COL, "rotated_buffer_sets": len(sets),
             "step_algorithmic_bytes": step_bytes,
+            "transform_overhead_bytes": transform_bytes,
         },
         "frac_of_peak": round(value / HBM_PEAK_GBPS, 4),
         "roofline": roofline,
         "cpu_baseline": cpu_baseline,
         "kernels": kernels,
+        "group_sweep": group_sweep,
+        "mx_tokens_shape": mx_tokens,
+        "group_scale_concurrency": concurrency,
         "variants": variants,
         "grouped_mm": grouped_mm,
         "kernels_method": "each call alone, back to back over the rotated buffer sets, events at both ends",
         "copy_ceiling_GBps": round(copy_gbps, 1),
-        "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""), "cus": props.multi_processor_count},
+        "device": device_facts(torch),
         "host_ms_per_step": round(host_ms, 4), "device_ms_per_step": round(dev_ms, 4),
     }
     print(json.dumps(out), flush=True)
