@@ -223,6 +223,28 @@ def test_hold_and_deferred_routes(route, group_knobs):
     check_group(x_bits, _sizes_to_ends([1000, 1000]), name=route + " with tail rows")
 
 
+@pytest.mark.parametrize("mode", ["hold", "twopass"])
+def test_every_finite_bf16_amax(mode, group_knobs):
+    """One column per |bf16| maximum 0x0000 .. 0x7F7F (every finite magnitude,
+    zero and subnormals included: 32640 columns), so the binary32 division
+    448 / max(amax, 1e-12) and the quantization relative to it are checked for
+    every possible amax, against the oracle, bit for bit.  Group 0 (24 rows): row
+    0 holds +amax(k) in column k, the other rows random bf16 patterns of no larger
+    magnitude with random signs; group 1 (24 rows) the same with amax(K-1-k),
+    negated in its first row."""
+    group_knobs(method=mode)
+    K, R = 32640, 24
+    rng = np.random.default_rng(5)
+    a0 = np.arange(K, dtype=np.int64)
+    a1 = a0[::-1].copy()
+    x = np.zeros((2 * R, K), np.uint16)
+    for g, a in enumerate((a0, a1)):
+        rows = rng.integers(0, a + 1, size=(R - 1, K)) | (rng.integers(0, 2, size=(R - 1, K)) << 15)
+        x[g * R] = a | (0x8000 if g == 1 else 0)
+        x[g * R + 1:(g + 1) * R] = rows.astype(np.uint16)
+    check_group(x, np.array([R, 2 * R], np.int32), name=f"every amax ({mode})")
+
+
 def test_concurrent_calls_on_separate_streams():
     """The library keeps no state: two group-scaling calls (hold method, row-major;
     two-pass, column-major) and an MX round trip in flight at once on three

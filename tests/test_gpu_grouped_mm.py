@@ -132,6 +132,13 @@ CASES = {
     "all_rows_in_no_group": (90, 72, 128, {"ends": [0, 0]}, 11),
     "decreasing_offsets": (600, 136, 256, {"ends": [300, 100, 500, 2000]}, 13),
     "min_n": (64, 8, 128, {"sizes": [10, 54]}, 15),
+    # K past one 1024-byte scale chunk: the two-slot scale ring wraps (K > 1024),
+    # including scale rows K/32 that are not a multiple of 16 (K = 640, 1152)
+    "k640_ragged": (520, 200, 640, {"sizes": [200, 0, 171, 9, 100]}, 17),       # 40 tail rows, N tail
+    "k1152_ragged": (390, 136, 1152, {"sizes": [1, 128, 250]}, 19),             # 11 tail rows
+    "k1536_two_groups": (300, 264, 1536, {"sizes": [129, 171]}, 21),
+    "k2048_ragged": (700, 264, 2048, {"sizes": [300, 0, 257, 1, 100]}, 23),     # 42 tail rows
+    "k5120_moe_width": (300, 200, 5120, {"sizes": [150, 0, 140]}, 25),          # the MoE hidden size, 10 tail rows
 }
 
 
