@@ -65,5 +65,28 @@ def build(verbose: bool = True) -> str:
     return LIB_PATH
 
 
+def build_host_asan(out_dir: str) -> str:
+    """libmxq with AddressSanitizer on the host code (device code as usual), for
+    the CPU tests of the C ABI's argument handling.  The sanitizer applies to the
+    host pass only (-Xarch_host); load the result with the ASan runtime preloaded."""
+    os.makedirs(out_dir, exist_ok=True)
+    flags = ["-O1", "-g", "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+    def one(src):
+        obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".o")
+        cmd = [hipcc(), *COMMON_FLAGS, *DEVICE_FLAGS, *flags, "-c", os.path.join(CSRC, src), "-o", obj]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"hipcc (host ASan) failed for {src}:\n{res.stderr[-2000:]}")
+        return obj
+
+    with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
+        objs = list(ex.map(one, SOURCES))
+    out = os.path.join(out_dir, "libmxq_host_asan.so")
+    subprocess.run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Xarch_host", "-fsanitize=address",
+                    *objs, "-o", out], check=True)
+    return out
+
+
 if __name__ == "__main__":
     build()

@@ -124,90 +124,4 @@ __device__ __forceinline__ int wave_incl_sum(int v)
 
 __device__ __forceinline__ int readlane(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
 
-// ------------------------------------------------------- token chunking ---
-//
-// Group g owns rows [end(g-1), end(g)) with end(g) = min(M, max(0, offs[0..g]))
-// (end(-1) = 0).  Pseudo-group G (when asked for) owns the rows past the last
-// end.  Every group is cut at the multiples of R, so a group [st, en) has
-// ceil(en/R) - floor(st/R) chunks (0 if empty), numbered consecutively over the
-// groups.  Aligned chunks keep full tiles aligned in both output layouts; the
-// total never exceeds ceil(M/R) + G.
-struct Chunk {
-    int g;    // group, G for the rows past the last end, -1 if the chunk id is unused
-    int r0;   // first row
-    int r1;   // one past the last row
-};
-
-// Executed by a whole wave (all 64 lanes active); the result is wave-uniform.
-template <int R>
-__device__ Chunk locate_chunk(const int32_t* __restrict__ offs, int G, int M, int j, bool with_tail)
-{
-    const int lane = lane_id();
-    const int ng = with_tail ? G + 1 : G;
-    int carry_end = 0, carry_cnt = 0;
-    for (int base = 0; base < ng; base += kWave) {
-        const int g = base + lane;
-        int e = (g < G) ? offs[g] : M;
-        e = e > 0 ? e : 0;
-        e = wave_incl_max(e);
-        e = e > carry_end ? e : carry_end;
-        e = e < M ? e : M;
-        int st = __shfl_up(e, 1, kWave);
-        if (lane == 0) st = carry_end;
-        const int cnt = (g < ng && e > st) ? ((e + R - 1) / R - st / R) : 0;
-        const int incl = wave_incl_sum(cnt) + carry_cnt;
-        const int excl = incl - cnt;
-        const unsigned long long hit = __ballot(cnt > 0 && j >= excl && j < incl);
-        if (hit) {
-            const int l = __builtin_ctzll(hit);
-            const int hst = readlane(st, l), hen = readlane(e, l), hexcl = readlane(excl, l);
-            const int i = j - hexcl;
-            const int a = (hst / R) * R;
-            Chunk c;
-            c.g = base + l;
-            c.r0 = hst > a + i * R ? hst : a + i * R;
-            c.r1 = hen < a + (i + 1) * R ? hen : a + (i + 1) * R;
-            return c;
-        }
-        carry_end = readlane(e, kWave - 1);
-        carry_cnt = readlane(incl, kWave - 1);
-    }
-    Chunk none;
-    none.g = -1;
-    none.r0 = 0;
-    none.r1 = 0;
-    return none;
-}
-
-// First chunk id and chunk count of group g (same numbering, no tail).
-template <int R>
-__device__ void group_chunk_span(const int32_t* __restrict__ offs, int G, int M, int gsel,
-                                 int* first, int* count)
-{
-    const int lane = lane_id();
-    int carry_end = 0, carry_cnt = 0;
-    for (int base = 0; base < G; base += kWave) {
-        const int g = base + lane;
-        int e = (g < G) ? offs[g] : M;
-        e = e > 0 ? e : 0;
-        e = wave_incl_max(e);
-        e = e > carry_end ? e : carry_end;
-        e = e < M ? e : M;
-        int st = __shfl_up(e, 1, kWave);
-        if (lane == 0) st = carry_end;
-        const int cnt = (g < G && e > st) ? ((e + R - 1) / R - st / R) : 0;
-        const int incl = wave_incl_sum(cnt) + carry_cnt;
-        if (gsel < base + kWave) {
-            const int l = gsel - base;
-            *count = readlane(cnt, l);
-            *first = readlane(incl, l) - *count;
-            return;
-        }
-        carry_end = readlane(e, kWave - 1);
-        carry_cnt = readlane(incl, kWave - 1);
-    }
-    *first = 0;
-    *count = 0;
-}
-
 }  // namespace mxq
