@@ -22,7 +22,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libmxq.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
-SOURCES = ["api.hip", "mx_codec.hip", "mx_dim0.hip", "dispatch.hip", "group_scale.hip", "transpose.hip",
+SOURCES = ["api.hip", "mx_codec.hip", "mx_dim0.hip", "dispatch.hip", "group_scale.hip", "group_split.hip", "transpose.hip",
            "grouped_mm.hip"]
 ARCH = "gfx950"
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -191,7 +191,7 @@ mxq_status mxq_group_scale_fp8_noalloc(const void* x_bf16, int64_t M, int64_t K,
 
 mxq_status mxq_set_group_scale_knobs(int method, int hold_tiles, int64_t wait_us, int strip_block)
 {
-    if (method < 0 || method > 2) return MXQ_ERR_RULE;
+    if (method < 0 || method > 3) return MXQ_ERR_RULE;
     mxq::set_group_scale_knobs(method, hold_tiles, wait_us < 0 ? -1 : (long)wait_us, strip_block);
     return MXQ_OK;
 }

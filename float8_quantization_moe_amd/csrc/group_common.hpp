@@ -135,17 +135,19 @@ __device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes)
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// `soff` is a wave-uniform byte offset carried in the instruction's scalar
+// offset field (no vector register for it).
 template <int POLICY = kNonTemporal>
-__device__ __forceinline__ uint4 buf_load16(Rsrc r, uint32_t off)
+__device__ __forceinline__ uint4 buf_load16(Rsrc r, uint32_t off, uint32_t soff = 0)
 {
-    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, POLICY);
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, POLICY);
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-__device__ __forceinline__ void buf_store8(uint2 v, Rsrc r, uint32_t off)
+__device__ __forceinline__ void buf_store8(uint2 v, Rsrc r, uint32_t off, uint32_t soff = 0)
 {
     const u32x2 w = {v.x, v.y};
-    __builtin_amdgcn_raw_buffer_store_b64(w, r, off, 0, kNonTemporal);
+    __builtin_amdgcn_raw_buffer_store_b64(w, r, off, soff, kNonTemporal);
 }
 
 // An opaque copy: the compiler cannot relate the result to its input, so

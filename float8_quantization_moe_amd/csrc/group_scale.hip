@@ -155,7 +155,9 @@ size_t group_scale_workspace_bytes(int64_t M, int64_t K, int32_t G)
     size_t off[10];
     const size_t a = workspace_layout<0>(M, K, G, off);
     const size_t b = workspace_layout<1>(M, K, G, off);
-    return a > b ? a : b;
+    const size_t c = group_split_sizes_ok(M, K, G) ? group_split_workspace_bytes(M, K, G) : 0;
+    const size_t ab = a > b ? a : b;
+    return ab > c ? ab : c;
 }
 
 // Everything a tile needs to know about itself.
@@ -985,14 +987,21 @@ static hipError_t launch_layout(const void* x, int M, int K, const int32_t* offs
     if (S % SB != 0) SB = S;
     const unsigned long long timeout_ticks =
         (unsigned long long)(di->rate_khz > 0 ? di->rate_khz : 100000) * (unsigned long long)wait_us / 1000ull;
-    // The method.  Default: hold, except for column-major output with more than
-    // a few groups, where the hold kernel's tiles cut at group boundaries split
-    // too many output lines (measured at 16640 x 5120: hold wins at 16 groups,
-    // two-pass from 32 on, so the switch is at about one group per five 128-row
-    // blocks).  Row-major output always holds.
+    // The method.  Default, from measurements at 16640 x 5120 (16 to 128 Zipf
+    // groups): row-major output holds (one read of X; 70-82 us against 74-103 us
+    // for either two-pass method).  Column-major output splits into two
+    // streaming passes while the average group spans at least two 128-row
+    // blocks (76-86 us against 81-105 us: the hold kernel's tiles, cut at group
+    // boundaries, split output lines, and the four-launch two-pass method pays
+    // two more kernel boundaries), and takes the four-launch two-pass method with
+    // more groups (90 us against 106 us: the split method's quantize pass then
+    // reduces several groups per block).
     bool twopass = LAYOUT == 1 && 5 * (int64_t)G >= (M + 127) / 128;
-    if (kn.method == 1) twopass = false;
-    if (kn.method == 2) twopass = true;
+    bool split = LAYOUT == 1 && 2 * (int64_t)G <= (M + 127) / 128 && group_split_sizes_ok(M, K, G);
+    if (kn.method == 1) twopass = split = false;
+    if (kn.method == 2) twopass = true, split = false;
+    if (kn.method == 3) split = group_split_sizes_ok(M, K, G);
+    if (split) return launch_group_split(x, M, K, offs, G, LAYOUT, flags, q, out_scales, workspace, stream);
 
     // the fills are a few MB: give them enough blocks (the scales are polled
     // only by the hold kernel)

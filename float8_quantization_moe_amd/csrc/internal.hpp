@@ -23,7 +23,11 @@ hipError_t launch_mx_dequantize(const void* q, const void* s, int64_t M, int64_t
 
 bool group_scale_sizes_ok(int64_t M, int64_t K, int64_t G);
 size_t group_scale_workspace_bytes(int64_t M, int64_t K, int32_t G);
-// Route overrides for tests (process-wide): method 0 auto, 1 hold, 2 two-pass;
+bool group_split_sizes_ok(int64_t M, int64_t K, int64_t G);
+size_t group_split_workspace_bytes(int64_t M, int64_t K, int32_t G);
+hipError_t launch_group_split(const void* x, int M, int K, const int32_t* offs, int G, int layout, int flags, void* q,
+                              float* scales, void* workspace, hipStream_t stream);
+// Route overrides for tests (process-wide): method 0 auto, 1 hold, 2 two-pass, 3 split;
 // hold_tiles < 0, wait_us < 0 and strip_block <= 0 select the defaults.
 void set_group_scale_knobs(int method, int hold_tiles, long wait_us, int strip_block);
 // The allocation-free variant's scratch: a static device array of this many

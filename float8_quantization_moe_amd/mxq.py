@@ -43,7 +43,7 @@ EXPORTED = ("mxq_abi_version", "mxq_status_string", "mxq_last_hip_error", "mxq_q
             "mxq_dispatch_pack_workspace_bytes", "mxq_dispatch_pack_mx", "mxq_scaled_grouped_mm_packed",
             "mxq_set_group_scale_knobs", "mxq_group_scale_fp8_noalloc")
 
-GROUP_METHODS = {"auto": 0, "hold": 1, "twopass": 2}
+GROUP_METHODS = {"auto": 0, "hold": 1, "twopass": 2, "split": 3}
 
 
 class MxqError(RuntimeError):

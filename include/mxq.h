@@ -208,12 +208,15 @@ size_t mxq_group_scale_workspace_bytes(int64_t M, int64_t K, int32_t G);
  * the tile count (about (M/128 + G) * K/512) below 2^31 (MXQ_ERR_SHAPE otherwise).
  * K == 0 is a no-op; M == 0 still writes the (G, K) scales.
  *
- * Two methods, picked on the host from the sizes alone: "hold" (X read once,
- * tiles held on chip until their group's scales are known) for row-major
- * output and for column-major output with fewer than one group per five
- * 128-row blocks, "two-pass" (an amax pass, then a quantize pass that reads X
- * again) otherwise.  Both give the same bytes; mxq_set_group_scale_knobs can
- * force either one.
+ Three methods, picked on the host from the sizes alone, all giving the same
+ * bytes (mxq_set_group_scale_knobs can force any of them):
+ *   "hold"    X read once, tiles held on chip until their group's scales are
+ *             known: row-major output;
+ *   "split"   two streaming launches (column maxima per 128-row block, then
+ *             reduce + quantize): column-major output while the average group
+ *             spans at least two 128-row blocks (needs G <= 256);
+ *   "two-pass" an amax pass, a finalize pass and a quantize pass: column-major
+ *             output with more groups.
  */
 mxq_status mxq_group_scale_fp8(const void* x_bf16, int64_t M, int64_t K,
                                const int32_t* group_end_offs, int32_t G, int out_layout,
@@ -266,7 +269,8 @@ mxq_status mxq_group_scale_fp8_noalloc(const void* x_bf16, int64_t M, int64_t K,
  * mxq_group_scale_fp8 / mxq_group_scale_fp8_ex route their work, for every
  * later call in the process (the bytes written never depend on it, only the
  * route and the speed).
- *   method       0 = automatic (the default), 1 = hold, 2 = two-pass.
+ *   method       0 = automatic (the default), 1 = hold, 2 = two-pass, 3 = split
+ *                (G <= 256; otherwise the automatic choice).
  *   hold_tiles   the hold method's limit on tiles of one group held on chip at
  *                once (larger groups go through its deferred pass); < 0 = the
  *                device's resident capacity less 16 (the default); 0 defers
@@ -276,7 +280,7 @@ mxq_status mxq_group_scale_fp8_noalloc(const void* x_bf16, int64_t M, int64_t K,
  *                fallback at once.
  *   strip_block  the hold method's launch order (strips per block of
  *                consecutive workgroups); <= 0 = 1 (the default).
- * MXQ_ERR_RULE for a method outside 0..2.  It is a process-wide setting that
+ * MXQ_ERR_RULE for a method outside 0..3.  It is a process-wide setting that
  * concurrent calls read without synchronisation: change it only while no
  * group-scaling call is being issued.
  */

@@ -137,7 +137,7 @@ def test_group_scale_argument_errors(L):
     assert na(A, 262144, 8192, A, 16, 0, 0, A, A, S) == 5         # needs more than the 16 MiB scratch
     assert na(A, 512, 0, A, 4, 0, 0, A, A, S) == 0                # K == 0: no-op
     k = L.mxq_set_group_scale_knobs                              # the route hook: method 0..2 only
-    assert k(3, -1, -1, 0) == 9 and k(-1, -1, -1, 0) == 9
+    assert k(4, -1, -1, 0) == 9 and k(-1, -1, -1, 0) == 9
     assert k(2, 5, 0, 2) == 0 and k(0, -1, -1, 0) == 0
     assert fx(A, 512, 256, A, 4, 0, -1, A, A, A, ws, S) == 9
     assert fx(A, 512, 256, A, 4, 2, 1, A, A, A, ws, S) == 4      # layout before flags

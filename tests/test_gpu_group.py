@@ -90,7 +90,7 @@ EDGE_CASES = {
 }
 
 
-MODES = ["hold", "twopass"]
+MODES = ["hold", "twopass", "split"]
 
 
 @pytest.mark.parametrize("mode", MODES)
@@ -223,7 +223,7 @@ def test_hold_and_deferred_routes(route, group_knobs):
     check_group(x_bits, _sizes_to_ends([1000, 1000]), name=route + " with tail rows")
 
 
-@pytest.mark.parametrize("mode", ["hold", "twopass"])
+@pytest.mark.parametrize("mode", ["hold", "twopass", "split"])
 def test_every_finite_bf16_amax(mode, group_knobs):
     """One column per |bf16| maximum 0x0000 .. 0x7F7F (every finite magnitude,
     zero and subnormals included: 32640 columns), so the binary32 division

@@ -95,7 +95,7 @@ EDGE = {
 }
 
 
-@pytest.mark.parametrize("mode", ["hold", "twopass"])
+@pytest.mark.parametrize("mode", ["hold", "twopass", "split"])
 @pytest.mark.parametrize("flags", FLAGS, ids=FIDS)
 @pytest.mark.parametrize("case", list(EDGE), ids=list(EDGE))
 def test_edge_cases(case, flags, mode, group_knobs):

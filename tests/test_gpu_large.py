@@ -92,7 +92,7 @@ def test_mx_dim0_past_2_31_elements(x):
     assert np.array_equal(gq, wq), U.first_mismatch(gq, wq)
 
 
-@pytest.mark.parametrize("mode", ["hold", "twopass"])
+@pytest.mark.parametrize("mode", ["hold", "twopass", "split"])
 def test_group_scaling_and_transform_past_2_31_elements(x, mode, group_knobs):
     """16 Zipf groups (the largest far beyond what one launch can hold, so the
     hold method streams it through its deferred pass), row-major and

@@ -88,7 +88,7 @@ def test_mx_dim0_random(seed):
     assert np.array_equal(U.host_u16(yg.t), oracle.mx_dequantize_ex(wq, ws, 0))
 
 
-@pytest.mark.parametrize("mode", ["hold", "twopass"])
+@pytest.mark.parametrize("mode", ["hold", "twopass", "split"])
 @pytest.mark.parametrize("seed", range(8))
 def test_group_scaling_random(seed, mode, group_knobs):
     group_knobs(method=mode)
