@@ -569,23 +569,33 @@ def main():
         st = launch_stats(torch, stream, fn, reps)
         mx_tokens[name] = {**st, **rate(mx_bytes(M2, K2), st["median_us"]), "shape": [M2, K2]}
     del xq_t, xs_t, y_t
-    # Group scaling (16 groups, row-major: the hold method, which keeps a group's
-    # tiles resident together) while a streaming copy of 2 GiB runs on a second
-    # stream of the same GPU, against the same call alone.
+    # Group scaling (16 groups, row-major) while a streaming copy of 2 GiB runs
+    # on a second stream of the same GPU, against the same call alone: the hold
+    # method (the default; it keeps a group's tiles resident together, so other
+    # work on the device can make its waits run out), with its route counters,
+    # and the two methods that never wait, forced through the tuning hook.
     side = torch.cuda.Stream()
     big_src = torch.empty(1 << 31, dtype=torch.uint8, device=dev)
     big_dst = torch.empty_like(big_src)
     g16 = lambda i: mxq.mxq_group_scale_fp8(sets[i % len(sets)].x2, offs16, ROW, sets[0].q2, sets[0].sc2, ws, stream)
-    alone = launch_stats(torch, stream, g16, 10)
-    torch.cuda.synchronize()
-    with torch.cuda.stream(side):
-        for _ in range(4):
-            big_dst.copy_(big_src)                        # about 4 x 0.8 ms of copying queued on the side stream
-    beside = launch_stats(torch, stream, g16, 10)         # issued at once, overlapping the copies
-    torch.cuda.synchronize()
     concurrency = {"what": ("group scaling (16640, 5120), 16 groups, row-major, while 2 GiB device copies run "
-                            "on a second stream; per-launch events on the call's stream"),
-                   "alone": alone, "beside_streaming_copy": beside}
+                            "on a second stream; per-launch events on the call's stream")}
+    for method in ("hold", "split", "twopass"):
+        with mxq.group_scale_knobs(method=method):
+            for i in range(2):
+                g16(i)
+            alone = launch_stats(torch, stream, g16, 10)
+            torch.cuda.synchronize()
+            with torch.cuda.stream(side):
+                for _ in range(4):
+                    big_dst.copy_(big_src)                # about 4 x 0.8 ms of copying queued on the side stream
+            beside = launch_stats(torch, stream, g16, 10)     # issued at once, overlapping the copies
+            entry = {"alone": alone, "beside_streaming_copy": beside}
+            if method == "hold":
+                t_out, reread = mxq.mxq_group_scale_route_counters(ws, M2, K2, len(ends16), ROW, stream)
+                entry["last_call_route_counters"] = {"timed_out_tiles": t_out, "tiles_reread_from_x": reread}
+            torch.cuda.synchronize()
+        concurrency[method] = entry
     del big_src, big_dst, side
     for i in range(2):
         step(i)

@@ -196,6 +196,18 @@ mxq_status mxq_set_group_scale_knobs(int method, int hold_tiles, int64_t wait_us
     return MXQ_OK;
 }
 
+mxq_status mxq_group_scale_route_counters(const void* workspace, size_t workspace_bytes, int64_t M, int64_t K,
+                                          int32_t G, int out_layout, uint32_t* counters, void* stream)
+{
+    mxq_status st = check_group_sizes(M, K, G);
+    if (st != MXQ_OK) return st;
+    if (out_layout != MXQ_LAYOUT_ROW && out_layout != MXQ_LAYOUT_COL) return MXQ_ERR_LAYOUT;
+    if (!counters) return MXQ_ERR_NULL;
+    if (!workspace || workspace_bytes < mxq::group_scale_workspace_bytes(M, K, G)) return MXQ_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return MXQ_ERR_ALIGN;
+    return hip_status(mxq::group_scale_route_counters(workspace, M, K, G, out_layout, counters, (hipStream_t)stream));
+}
+
 mxq_status mxq_transpose_u8(const void* in, int64_t R, int64_t C, void* out, void* stream)
 {
     mxq_status st = check_2d(R, C);

@@ -109,6 +109,8 @@ struct Workspace {
     int32_t* bfirst;      // [ceil(M/128)] group containing the first row of each 128-row block (G: none)
     uint32_t* deferred;   // [slots][S] 1 if the tile was left for the deferred kernel
     uint32_t* any;        // [1] 1 if any tile needs the deferred kernel
+    uint32_t* stats;      // [2] route counters: tiles whose wait for their scales ran out;
+                          // tile-sized pieces (128 rows x one strip) read again from the input
     float* inv_out;       // the caller's (G, K) scales when they hold 1/s (the kernels then keep the
                           // multipliers s in a workspace array); NULL when they hold s itself
     int pow2;             // 1: multipliers rounded down to a power of two
@@ -318,7 +320,11 @@ void group_plan_kernel(const int32_t* __restrict__ offs, int G, int M, int K, Wo
     for (int i = tid; i < nScale16; i += stride) ((uint4*)scales)[i] = s_unset;
     for (int i = tid; i < nGS; i += stride) ws.count[i] = 0;
     for (int i = tid; i < nTiles; i += stride) ws.deferred[i] = 0;
-    if (tid == 0) *ws.any = 0;
+    if (tid == 0) {
+        *ws.any = 0;
+        ws.stats[0] = 0;
+        ws.stats[1] = 0;
+    }
     if (blockIdx.x != 0) return;
 
     __shared__ int sh_st[kWave], sh_en[kWave], sh_first[kWave], sh_cnt[kWave];
@@ -504,14 +510,60 @@ __device__ __forceinline__ int publish_and_count(const uint4 (&v)[TileCfg<LAYOUT
     return sh.state;
 }
 
+// The strip's scales from its column maxima `a` (rs == 0 lanes: their 8
+// columns over their rows; all lanes' values are combined through LDS): divide,
+// store them (`publish`: with agent-scope stores, for readers in the same
+// launch) and leave this lane's 8 scales in `cs`.
+template <int LAYOUT, class Sh>
+__device__ __forceinline__ void finish_strip(uint4 a, const TileInfo& t, int K, int k, int cg, int rs,
+                                             const Workspace& ws, float* __restrict__ scales, bool publish, Sh& sh,
+                                             ColScales& cs)
+{
+    using C = TileCfg<LAYOUT>;
+    sh.red[rs][cg] = a;
+    __syncthreads();
+    if (rs == 0) {
+        max_rows(a, &sh.red[0][cg], C::NS, C::CG);
+        const float4 lo = scales_lo(a, ws.pow2), hi = scales_hi(a, ws.pow2);
+        *(float4*)(sh.scale + cg * 8) = lo;
+        *(float4*)(sh.scale + cg * 8 + 4) = hi;
+        if (k < K) {
+            float* dst = scales + (int64_t)t.g * K + k;
+            if (publish) {
+                store_coherent(f4_bits(lo), dst);
+                store_coherent(f4_bits(hi), dst + 4);
+            } else {
+                *(float4*)dst = lo;
+                *(float4*)(dst + 4) = hi;
+            }
+            if (ws.inv_out) {                              // the caller's 1/s (read by no kernel)
+                *(float4*)(ws.inv_out + (int64_t)t.g * K + k) = inverse4(lo);
+                *(float4*)(ws.inv_out + (int64_t)t.g * K + k + 4) = inverse4(hi);
+            }
+        }
+    }
+    __syncthreads();
+    cs = make_col_scales(*(const float4*)(sh.scale + cg * 8), *(const float4*)(sh.scale + cg * 8 + 4));
+}
+
+// The strip's column maxima over all of the group's rows, read from the input
+// (only when a wait ran out); counted in the route counters as the group's
+// chunk count.
+template <int LAYOUT>
+__device__ __forceinline__ uint4 strip_max_fallback(const uint16_t* __restrict__ x, const TileInfo& t, int K, int k,
+                                                    int rs, const Workspace& ws)
+{
+    if (threadIdx.x == 0)
+        __hip_atomic_fetch_add(ws.stats + 1, (uint32_t)t.count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return strip_max_from_x(x, K, t, k, rs, TileCfg<LAYOUT>::NS);
+}
+
 // Reduce the strip's partial rows over the group's chunks, except chunk `skip`
-// whose maxima the rs == 0 lanes bring in `own` (zeros otherwise), divide,
-// store the scales (`scales_coherent`: with agent-scope stores, for readers in
-// the same launch) and leave this lane's 8 scales in `cs`.  Each lane polls its
-// rows in batches: every round trip re-reads all rows of the batch not yet
-// written, so the batch completes one round trip after its last row lands.  If
-// a row does not come within the time limit, the maxima are taken from the
-// input instead.
+// whose maxima the rs == 0 lanes bring in `own` (zeros otherwise), then finish
+// the strip.  Each lane polls its rows in batches: every round trip re-reads all
+// rows of the batch not yet written, so the batch completes one round trip after
+// its last row lands.  If a row does not come within the time limit, the maxima
+// are taken from the input instead.
 constexpr int kPollBatch = 4;
 template <int LAYOUT, class Sh>
 __device__ __forceinline__ void reduce_strip(const uint16_t* __restrict__ x, const TileInfo& t, int K, int k, int cg,
@@ -558,31 +610,71 @@ __device__ __forceinline__ void reduce_strip(const uint16_t* __restrict__ x, con
             }
         }
     }
-    if (__syncthreads_or(!ok)) a = strip_max_from_x(x, K, t, k, rs, C::NS);   // a partial never came
-    sh.red[rs][cg] = a;
-    __syncthreads();
-    if (rs == 0) {
-        max_rows(a, &sh.red[0][cg], C::NS, C::CG);
-        const float4 lo = scales_lo(a, ws.pow2), hi = scales_hi(a, ws.pow2);
-        *(float4*)(sh.scale + cg * 8) = lo;
-        *(float4*)(sh.scale + cg * 8 + 4) = hi;
-        if (k < K) {
-            float* dst = scales + (int64_t)t.g * K + k;
-            if (scales_coherent) {
-                store_coherent(f4_bits(lo), dst);
-                store_coherent(f4_bits(hi), dst + 4);
-            } else {
-                *(float4*)dst = lo;
-                *(float4*)(dst + 4) = hi;
-            }
-            if (ws.inv_out) {                              // the caller's 1/s (read by no kernel)
-                *(float4*)(ws.inv_out + (int64_t)t.g * K + k) = inverse4(lo);
-                *(float4*)(ws.inv_out + (int64_t)t.g * K + k + 4) = inverse4(hi);
+    if (__syncthreads_or(!ok)) a = strip_max_fallback<LAYOUT>(x, t, K, k, rs, ws);   // a partial never came
+    finish_strip<LAYOUT>(a, t, K, k, cg, rs, ws, scales, scales_coherent, sh, cs);
+}
+
+// The rs == 0 lanes poll their 8 scales until written or until `ticks` have
+// passed, and pass them on through LDS.  Returns false (in every lane) if any
+// lane's wait ran out.
+template <class Sh>
+__device__ __forceinline__ bool wait_scales(const float* __restrict__ scales, const TileInfo& t, int K, int k, int cg,
+                                            int rs, unsigned long long ticks, Sh& sh)
+{
+    int ok = 1;
+    if (rs == 0 && k < K) {
+        const float* sp = scales + (int64_t)t.g * K + k;
+        uint4 s0 = load_coherent(sp), s1 = load_coherent(sp + 4);
+        if (!scales_written(s0, s1)) {
+            const unsigned long long t0 = wall_clock64();
+            while (true) {
+                __builtin_amdgcn_s_sleep(2);
+                s0 = load_coherent(sp);
+                s1 = load_coherent(sp + 4);
+                if (scales_written(s0, s1)) break;
+                if (wall_clock64() - t0 > ticks) {
+                    ok = 0;
+                    break;
+                }
             }
         }
+        *(float4*)(sh.scale + cg * 8) = bits_f4(s0);
+        *(float4*)(sh.scale + cg * 8 + 4) = bits_f4(s1);
     }
+    return !__syncthreads_or(!ok);
+}
+
+// Chunk `jc`'s partial row, computed from the input and published (agent
+// scope) unless it is written already: the column maxima of the chunk's rows,
+// the same values its own tile publishes.  Counted in the route counters.
+template <int LAYOUT, class Sh>
+__device__ __forceinline__ void publish_chunk_if_missing(const uint16_t* __restrict__ x, const Workspace& ws, int jc,
+                                                         int K, int k, int cg, int rs, Sh& sh)
+{
+    using C = TileCfg<LAYOUT>;
+    uint16_t* dst = ws.partial + (int64_t)jc * K + k;
+    const bool missing = rs == 0 && k < K && !partial_written(load_coherent(dst));
+    if (!__syncthreads_or(missing)) return;
+    const int4 e = *(const int4*)(ws.table + jc);         // group, rows [r0, r1) (at most R), first chunk
+    uint4 m = make_uint4(0, 0, 0, 0);
+    if (k < K) {
+        uint4 b[C::H];
+#pragma unroll
+        for (int i = 0; i < C::H; ++i) {
+            const int r = e.y + rs + C::NS * i;
+            b[i] = r < e.z ? *(const uint4*)(x + (int64_t)r * K + k) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < C::H; ++i) max8(m, abs8(b[i]));
+    }
+    sh.red[rs][cg] = m;
     __syncthreads();
-    cs = make_col_scales(*(const float4*)(sh.scale + cg * 8), *(const float4*)(sh.scale + cg * 8 + 4));
+    if (rs == 0) {
+        max_rows(m, &sh.red[0][cg], C::NS, C::CG);
+        if (k < K) store_coherent(m, dst);
+    }
+    if (threadIdx.x == 0) __hip_atomic_fetch_add(ws.stats + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
 }
 
 // ---------------------------------------------------------------- hold ----
@@ -590,7 +682,7 @@ template <int LAYOUT>
 __global__ __launch_bounds__(TileCfg<LAYOUT>::T)
 void group_hold_kernel(const uint16_t* __restrict__ x, int M, int K, int G, int S, int SB, int slots, Workspace ws,
                        float* __restrict__ scales, uint8_t* __restrict__ q, int hold_limit,
-                       unsigned long long timeout_ticks, int deferred_launched)
+                       unsigned long long timeout_ticks, unsigned long long rescue_ticks, int deferred_launched)
 {
     using C = TileCfg<LAYOUT>;
     __shared__ TileShared<LAYOUT> sh;
@@ -627,29 +719,9 @@ void group_hold_kernel(const uint16_t* __restrict__ x, int M, int K, int G, int 
     if (j == t.first + t.count - 1) {
         reduce_strip<LAYOUT>(x, t, K, k, cg, rs, ws, scales, j, own, true, timeout_ticks, sh, cs);
     } else {
-        // wait for the strip's scales: the rs == 0 lanes poll their 8 columns
-        // (bounded in wall-clock time) and pass them on through LDS
-        int ok = 1;
-        if (rs == 0 && k < K) {
-            const float* sp = scales + (int64_t)t.g * K + k;
-            uint4 s0 = load_coherent(sp), s1 = load_coherent(sp + 4);
-            if (!scales_written(s0, s1)) {
-                const unsigned long long t0 = wall_clock64();
-                while (true) {
-                    __builtin_amdgcn_s_sleep(2);
-                    s0 = load_coherent(sp);
-                    s1 = load_coherent(sp + 4);
-                    if (scales_written(s0, s1)) break;
-                    if (wall_clock64() - t0 > timeout_ticks) {
-                        ok = 0;
-                        break;
-                    }
-                }
-            }
-            *(float4*)(sh.scale + cg * 8) = bits_f4(s0);
-            *(float4*)(sh.scale + cg * 8 + 4) = bits_f4(s1);
-        }
-        if (__syncthreads_or(!ok)) {
+        // wait for the strip's scales (bounded in wall-clock time)
+        if (!wait_scales(scales, t, K, k, cg, rs, timeout_ticks, sh)) {
+            if (threadIdx.x == 0) __hip_atomic_fetch_add(ws.stats, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             if (deferred_launched) {
                 // left for the deferred kernel, which runs after every strip is reduced
                 if (threadIdx.x == 0) {
@@ -658,20 +730,40 @@ void group_hold_kernel(const uint16_t* __restrict__ x, int M, int K, int G, int 
                 }
                 return;
             }
-            // The wait ran out and no deferred pass follows: reduce this strip's
-            // maxima over all of the group's rows straight from the input (slow,
-            // only when the device cannot keep the group's tiles resident).
-            uint4 a = strip_max_from_x(x, K, t, k, rs, C::NS);
-            sh.red[rs][cg] = a;
-            __syncthreads();
-            if (rs == 0) {
-                max_rows(a, &sh.red[0][cg], C::NS, C::CG);
-                *(float4*)(sh.scale + cg * 8) = scales_lo(a, ws.pow2);
-                *(float4*)(sh.scale + cg * 8 + 4) = scales_hi(a, ws.pow2);
+            // The wait ran out and no deferred pass follows: some of the group's
+            // tiles are not running (the device, perhaps shared with other work,
+            // did not keep them resident together).  The tiles whose wait ran out
+            // take the strip's chunks one by one, from the last down, through
+            // the strip's arrival counter (unused for held groups); each chunk
+            // whose partial row is not written yet is computed from the input and
+            // published, as its own tile would.  Then every partial row comes
+            // from a running workgroup that waits for nothing, the first of these
+            // tiles reduces the strip and publishes the scales, and the others
+            // wait for them (the group's last tile, when it runs, publishes the
+            // same values).
+            bool first_helper = false;
+            for (int grab = 0;; ++grab) {
+                if (threadIdx.x == 0)
+                    sh.state = (int)__hip_atomic_fetch_add(ws.count + (int64_t)t.g * S + s, 1u, __ATOMIC_RELAXED,
+                                                           __HIP_MEMORY_SCOPE_AGENT);
+                __syncthreads();
+                const int n = sh.state;
+                __syncthreads();                          // (sh.state is written again by the next grab)
+                if (grab == 0) first_helper = n == 0;
+                if (n >= t.count) break;
+                publish_chunk_if_missing<LAYOUT>(x, ws, t.first + t.count - 1 - n, K, k, cg, rs, sh);
             }
-            __syncthreads();
+            if (first_helper)
+                reduce_strip<LAYOUT>(x, t, K, k, cg, rs, ws, scales, -1, make_uint4(0, 0, 0, 0), true,
+                                     timeout_ticks + rescue_ticks, sh, cs);
+            else if (!wait_scales(scales, t, K, k, cg, rs, timeout_ticks + rescue_ticks, sh))
+                finish_strip<LAYOUT>(strip_max_fallback<LAYOUT>(x, t, K, k, rs, ws), t, K, k, cg, rs, ws, scales, true,
+                                     sh, cs);
+            else
+                cs = make_col_scales(*(const float4*)(sh.scale + cg * 8), *(const float4*)(sh.scale + cg * 8 + 4));
+        } else {
+            cs = make_col_scales(*(const float4*)(sh.scale + cg * 8), *(const float4*)(sh.scale + cg * 8 + 4));
         }
-        cs = make_col_scales(*(const float4*)(sh.scale + cg * 8), *(const float4*)(sh.scale + cg * 8 + 4));
     }
     quantize_store_tile<LAYOUT>(v, cs, t, M, K, k, cg, rs, q, sh.stage, false);
 }
@@ -960,6 +1052,7 @@ static hipError_t launch_layout(const void* x, int M, int K, const int32_t* offs
     ws.empty = (uint32_t*)(base + off[3]);
     ws.deferred = (uint32_t*)(base + off[4]);
     ws.any = (uint32_t*)(base + off[5]);
+    ws.stats = ws.any + 1;
     ws.gend = (int32_t*)(base + off[6]);
     ws.bfirst = (int32_t*)(base + off[7]);
     ws.gchunks = (int32_t*)(base + off[8]);
@@ -985,8 +1078,11 @@ static hipError_t launch_layout(const void* x, int M, int K, const int32_t* offs
     const long wait_us = kn.wait_us >= 0 ? kn.wait_us : 2000;
     int SB = kn.strip_block > 0 ? kn.strip_block : 1;     // chunk-fastest launch order (measured best)
     if (S % SB != 0) SB = S;
-    const unsigned long long timeout_ticks =
-        (unsigned long long)(di->rate_khz > 0 ? di->rate_khz : 100000) * (unsigned long long)wait_us / 1000ull;
+    const unsigned long long ticks_per_ms = (unsigned long long)(di->rate_khz > 0 ? di->rate_khz : 100000);
+    const unsigned long long timeout_ticks = ticks_per_ms * (unsigned long long)wait_us / 1000ull;
+    // how much longer tiles wait for a strip claimed after a time-out (its
+    // claimant reads the group's rows of the strip, one workgroup alone)
+    const unsigned long long rescue_ticks = ticks_per_ms * 50ull;
     // The method.  Default, from measurements at 16640 x 5120 (16 to 128 Zipf
     // groups): row-major output holds (one read of X; 70-82 us against 74-103 us
     // for either two-pass method).  Column-major output splits into two
@@ -1032,7 +1128,7 @@ static hipError_t launch_layout(const void* x, int M, int K, const int32_t* offs
         const int deferred = (int64_t)(M + C::R - 1) / C::R + 1 > hold_limit ? 1 : 0;
         hipLaunchKernelGGL(group_hold_kernel<LAYOUT>, dim3((unsigned)nTiles), dim3(C::T), 0, stream,
                            (const uint16_t*)x, M, K, G, S, SB, (int)slots, ws, scales, (uint8_t*)q, hold_limit,
-                           timeout_ticks, deferred);
+                           timeout_ticks, rescue_ticks, deferred);
         if (!deferred) return hipGetLastError();
         const int dgrid = (int)(nTiles < 512 ? nTiles : 512);
         hipLaunchKernelGGL(group_deferred_kernel<LAYOUT>, dim3((unsigned)dgrid), dim3(C::T), 0, stream,
@@ -1069,6 +1165,19 @@ hipError_t group_scale_scratch(void** ptr)
     if (g_scratch_err[dev] != hipSuccess) return g_scratch_err[dev];
     *ptr = g_scratch_ptr[dev];
     return hipSuccess;
+}
+
+hipError_t group_scale_route_counters(const void* workspace, int64_t M, int64_t K, int64_t G, int layout,
+                                     uint32_t* out, hipStream_t stream)
+{
+    size_t off[10];
+    if (layout == 0)
+        workspace_layout<0>(M, K, G, off);
+    else
+        workspace_layout<1>(M, K, G, off);
+    const hipError_t e = hipMemcpyAsync(out, (const uint8_t*)workspace + off[5] + 4, 2 * sizeof(uint32_t),
+                                        hipMemcpyDeviceToHost, stream);
+    return e != hipSuccess ? e : hipStreamSynchronize(stream);
 }
 
 hipError_t launch_group_scale(const void* x, int M, int K, const int32_t* offs, int G, int layout, int flags,

@@ -34,6 +34,10 @@ void set_group_scale_knobs(int method, int hold_tiles, long wait_us, int strip_b
 // bytes per device, its address on the current device.
 constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
 hipError_t group_scale_scratch(void** ptr);
+// The hold method's route counters of the last call that used this workspace
+// (synchronises the stream).
+hipError_t group_scale_route_counters(const void* workspace, int64_t M, int64_t K, int64_t G, int layout,
+                                     uint32_t* out, hipStream_t stream);
 hipError_t launch_group_scale(const void* x, int M, int K, const int32_t* offs, int G, int layout, int flags,
                               void* q, float* scales, void* workspace, hipStream_t stream);
 

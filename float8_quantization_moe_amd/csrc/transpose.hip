@@ -12,8 +12,13 @@
 // contiguous bytes per output row.  Edge tiles and widths that are not a multiple
 // of 16 fall back to byte accesses for the affected pieces.  The 16-byte loads
 // and stores use the streaming (non-temporal) policy: every byte is touched once
-// (measured 35.5 -> 33.3 us at 5120 x 16640; wider or taller tiles, 128 x 256 up
-// to 256 x 256, measured the same).
+// (measured 35.5 -> 33.3 us at 5120 x 16640).  Consecutive workgroups take
+// consecutive tiles down a tile column, so the workgroups running at once
+// (one per XCD in turn) write adjacent pieces of the same output rows (33.0 ->
+// 31.5 us; 128 x 256 tiles, two tiles per workgroup and 2-D super-tile orders
+// measured the same or slower).  At that point the reads alone run at 78 % and
+// the writes alone at 72 % of the HBM peak: the transpose moves as many bytes
+// each way, and the turnaround between the two is what is left.
 #include "device_common.hpp"
 #include "internal.hpp"
 
@@ -22,17 +27,20 @@ namespace mxq {
 constexpr int kTThreads = 256;
 constexpr int kTile = 128;
 
+// Tile byte (column c, row r): each column's 128 bytes are 8 16-byte pieces,
+// permuted by c >> 4 so that the 8 lanes of a half-wave writing the same row
+// offset of 8 columns 16 apart hit 8 different pieces (32 different banks).
 __device__ __forceinline__ int ttile_offset(int c, int r)
 {
-    return c * kTile + ((((r >> 4) ^ (c >> 3)) & 7) << 4) + (r & 15);
+    return c * kTile + ((((r >> 4) ^ (c >> 4)) & 7) << 4) + (r & 15);
 }
 
 __global__ __launch_bounds__(kTThreads)
 void transpose_u8_kernel(const uint8_t* __restrict__ in, int64_t R, int64_t C, uint8_t* __restrict__ out,
-                         int64_t tiles_c)
+                         int64_t tiles_r)
 {
     __shared__ __align__(16) uint8_t tile[kTile * kTile];
-    const int64_t ti = (int64_t)blockIdx.x / tiles_c, tj = (int64_t)blockIdx.x % tiles_c;
+    const int64_t ti = (int64_t)blockIdx.x % tiles_r, tj = (int64_t)blockIdx.x / tiles_r;
     const int64_t i0 = ti * kTile, j0 = tj * kTile;
     const int t = (int)threadIdx.x;
     const int cg = t & 7;          // 16-byte column group, 0..7
@@ -94,7 +102,7 @@ hipError_t launch_transpose_u8(const void* in, int64_t R, int64_t C, void* out, 
 {
     const int64_t tiles_r = (R + kTile - 1) / kTile, tiles_c = (C + kTile - 1) / kTile;
     hipLaunchKernelGGL(transpose_u8_kernel, dim3((unsigned)(tiles_r * tiles_c)), dim3(kTThreads), 0, stream,
-                       (const uint8_t*)in, R, C, (uint8_t*)out, tiles_c);
+                       (const uint8_t*)in, R, C, (uint8_t*)out, tiles_r);
     return hipGetLastError();
 }
 

@@ -41,7 +41,7 @@ EXPORTED = ("mxq_abi_version", "mxq_status_string", "mxq_last_hip_error", "mxq_q
             "mxq_transpose_u8", "mxq_grouped_mm_workspace_bytes", "mxq_scaled_grouped_mm",
             "mxq_quantize_mx_ex", "mxq_dequantize_mx_ex", "mxq_group_scale_fp8_ex",
             "mxq_dispatch_pack_workspace_bytes", "mxq_dispatch_pack_mx", "mxq_scaled_grouped_mm_packed",
-            "mxq_set_group_scale_knobs", "mxq_group_scale_fp8_noalloc")
+            "mxq_set_group_scale_knobs", "mxq_group_scale_fp8_noalloc", "mxq_group_scale_route_counters")
 
 GROUP_METHODS = {"auto": 0, "hold": 1, "twopass": 2, "split": 3}
 
@@ -101,6 +101,8 @@ def lib() -> ctypes.CDLL:
         L.mxq_group_scale_fp8_noalloc.argtypes = [P, i64, i64, P, i32, ctypes.c_int, ctypes.c_int, P, P, P]
         L.mxq_set_group_scale_knobs.restype = ctypes.c_int
         L.mxq_set_group_scale_knobs.argtypes = [ctypes.c_int, ctypes.c_int, i64, ctypes.c_int]
+        L.mxq_group_scale_route_counters.restype = ctypes.c_int
+        L.mxq_group_scale_route_counters.argtypes = [P, sz, i64, i64, i32, ctypes.c_int, P, P]
         L.mxq_scaled_grouped_mm.restype = ctypes.c_int
         L.mxq_scaled_grouped_mm.argtypes = [P, P, P, P, P, i64, i64, i64, i32, ctypes.c_int, P, P, sz, P]
         _lib = L
@@ -112,6 +114,18 @@ def mxq_set_group_scale_knobs(method: str = "auto", hold_tiles: int = -1, wait_u
     """Test hook: force the group-scaling route (see include/mxq.h).  Defaults restore the automatic choice."""
     _check(lib().mxq_set_group_scale_knobs(GROUP_METHODS[method], int(hold_tiles), int(wait_us), int(strip_block)),
            "mxq_set_group_scale_knobs")
+
+
+def mxq_group_scale_route_counters(workspace: torch.Tensor, M: int, K: int, G: int, out_layout: int,
+                                   stream=None) -> tuple:
+    """Test hook: the hold method's (timed-out tiles, strips re-read from X) of the
+    last call that used `workspace` (see include/mxq.h).  Synchronises the stream."""
+    out = (ctypes.c_uint32 * 2)()
+    pw = _dev(workspace, "workspace")
+    wbytes = workspace.numel() * workspace.element_size()
+    _check(lib().mxq_group_scale_route_counters(pw, wbytes, int(M), int(K), int(G), int(out_layout), out,
+                                                _stream(stream)), "mxq_group_scale_route_counters")
+    return int(out[0]), int(out[1])
 
 
 @contextlib.contextmanager

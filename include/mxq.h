@@ -287,6 +287,22 @@ mxq_status mxq_group_scale_fp8_noalloc(const void* x_bf16, int64_t M, int64_t K,
 mxq_status mxq_set_group_scale_knobs(int method, int hold_tiles, int64_t wait_us, int strip_block);
 
 /*
+ * Test and tuning hook, not for production code: the hold method's route
+ * counters from the last mxq_group_scale_fp8 / _ex call that used `workspace`
+ * with these sizes and layout, read after synchronising `stream`:
+ *   counters[0]  tiles whose wait for their group's scales ran out (they then
+ *                went to the deferred pass, or to a strip rescue: the first such
+ *                tile of a (group, strip) reads the strip's maxima from X once
+ *                and publishes the scales, and the others wait for those);
+ *   counters[1]  strips whose maxima were read again from X.
+ * Both are 0 when every group's tiles were resident together.  Meaningless
+ * after a call that took another method, or with M == 0 or K == 0.  Argument
+ * errors as mxq_group_scale_fp8 (MXQ_ERR_NULL for counters == NULL).
+ */
+mxq_status mxq_group_scale_route_counters(const void* workspace, size_t workspace_bytes, int64_t M, int64_t K,
+                                          int32_t G, int out_layout, uint32_t* counters, void* stream);
+
+/*
  * Byte transpose: out (C, R) = in (R, C)^T, both row-major.  The layout
  * transform between the two outputs of mxq_group_scale_fp8.
  * Source: "[moe training] fix uncoalesced global accesses in per group rowwise

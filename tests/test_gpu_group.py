@@ -28,6 +28,10 @@ def gpu():
     yield
 
 
+# (layout, (timed-out tiles, tile-sized pieces re-read from X)) of every run_group call
+ROUTE_COUNTERS = []
+
+
 def run_group(x_bits, ends, layout, x_dev=None):
     M, K = x_bits.shape
     G = len(ends)
@@ -40,6 +44,8 @@ def run_group(x_bits, ends, layout, x_dev=None):
     mxq.mxq_group_scale_fp8(x, offs, layout, qg.t, sg.t, ws)
     torch.cuda.synchronize()
     assert qg.guard_intact() and sg.guard_intact(), "wrote past the end"
+    if M > 0 and K > 0:
+        ROUTE_COUNTERS.append((layout, mxq.mxq_group_scale_route_counters(ws, M, K, G, layout)))
     return U.host_u8(qg.t), U.host_f32_bits(sg.t)
 
 
@@ -210,17 +216,62 @@ ROUTES = {
 }
 
 
+def _tile_count(ends, M, K):
+    """Tiles (128-row chunks of a group x 512-column strips) of the hold method."""
+    st, n = 0, 0
+    for e in list(ends) + [M]:
+        e = min(max(int(e), st), M)
+        if e > st:
+            n += (e + 127) // 128 - st // 128
+        st = e
+    return n * ((K + 511) // 512)
+
+
 @pytest.mark.parametrize("route", list(ROUTES), ids=list(ROUTES))
 def test_hold_and_deferred_routes(route, group_knobs):
+    """Every route gives the oracle's bytes; the hold method's route counters
+    show the route was taken (no wait runs out when the tiles are resident; with
+    a zero wait they do, and the input re-read stays within two reads of each
+    tile)."""
     group_knobs(**ROUTES[route])
     M, K = 3000, 1040
     rng = np.random.default_rng(31)
     x = (rng.standard_normal((M, K)) * np.exp(rng.standard_normal((M, 1)))).astype(np.float32)
     x_bits = (x.view(np.uint32) >> 16).astype(np.uint16)
     x_bits[17, 5] = 0x7F80                 # a non-finite column in the first group
-    ends = _sizes_to_ends([1500, 0, 700, 3, 597, 200])   # all 3000 rows in groups
-    check_group(x_bits, ends, name=route)
-    check_group(x_bits, _sizes_to_ends([1000, 1000]), name=route + " with tail rows")
+    cases = [(_sizes_to_ends([1500, 0, 700, 3, 597, 200]), ""),    # all 3000 rows in groups
+             (_sizes_to_ends([1000, 1000]), " with tail rows")]
+    ROUTE_COUNTERS.clear()
+    for ends, what in cases:
+        check_group(x_bits, ends, name=route + what)
+    if route == "twopass":
+        return
+    timed_out = sum(c[0] for _, c in ROUTE_COUNTERS)
+    reread = sum(c[1] for _, c in ROUTE_COUNTERS)
+    tiles = sum(2 * _tile_count(e, M, K) for e, _ in cases)      # both layouts
+    if ROUTES[route].get("wait_us") == 0:
+        assert timed_out > 0, (route, ROUTE_COUNTERS)
+        assert reread <= 2 * tiles, (route, ROUTE_COUNTERS)
+    else:
+        assert timed_out == 0 and reread == 0, (route, ROUTE_COUNTERS)
+
+
+def test_group_larger_than_the_device_holds(group_knobs):
+    """One group of 2048 chunks (262144 rows x 512 columns) held on purpose
+    (the hold limit lifted, no deferred pass) while only about 512 tiles fit on
+    the device: the resident tiles' waits run out, they compute the missing
+    chunks' maxima from the input and publish the scales, and the rest of the
+    group then finds its scales written.  Bytes as the oracle's; the input is
+    read again at most once per tile beyond the strip's own reduction."""
+    group_knobs(method="hold", hold_tiles=1 << 30, wait_us=100)
+    M, K = 262144, 512
+    x_bits = W.bf16_bits(W.lognormal_rows(M, K, seed=91).to(torch.bfloat16))
+    ends = np.array([M], np.int32)
+    ROUTE_COUNTERS.clear()
+    check_group(x_bits, ends, name="one group of 2048 chunks")
+    for layout, (timed_out, reread) in ROUTE_COUNTERS:
+        assert timed_out > 0, (layout, timed_out, reread)
+        assert reread <= 2 * 2048, (layout, timed_out, reread)
 
 
 @pytest.mark.parametrize("mode", ["hold", "twopass", "split"])
