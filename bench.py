@@ -98,92 +98,184 @@ COPY_KERNEL = "__amd_rocclr_copyBuffer"
 COPY_BYTES = 1 << 30       # the 1 GiB device copies of the streaming-ceiling leg
 
 
+def _cdiv(a, b):
+    return -(-a // b)
+
+
+# Launch grids (work-items) of the kernels the bench runs, from the launch
+# configurations in csrc/: they tell apart dispatches of one kernel at different
+# sizes in the profiler's per-dispatch records.
+def grid_mx(M, K):                 # flat codec: 1024 16-byte chunks per 256-thread workgroup
+    return min(_cdiv(M * K // 8, 1024), 1 << 22) * 256
+
+
+def grid_dim0(M, K):               # 32 rows x 1024 columns per 256-thread workgroup
+    return (M // 32) * _cdiv(K, 1024) * 256
+
+
+def grid_transpose(R, C):          # 128 x 128-byte tiles, 256 threads
+    return _cdiv(R, 128) * _cdiv(C, 128) * 256
+
+
+def grid_hold(M, K, G):            # (128-row chunks + G + 1 slots) x 512-column strips, 512 threads
+    return (_cdiv(M, 128) + G + 1) * _cdiv(K, 512) * 512
+
+
+def grid_finalize(K, G):           # (group, 128-column strip), 256 threads
+    return G * _cdiv(K, 128) * 256
+
+
+def grid_col_blocks(M, K):         # 128-row blocks x 512-column strips, 512 threads
+    return _cdiv(M, 128) * _cdiv(K, 512) * 512
+
+
+def grid_split_amax(M, K):         # 128-row blocks x 256-column tiles, 256 threads
+    return _cdiv(M, 128) * _cdiv(K, 256) * 256
+
+
+def grid_split_quant(M, K):        # 128-row blocks x 128-column tiles, 256 threads
+    return _cdiv(M, 128) * _cdiv(K, 128) * 256
+
+
 def ingest_counters(stats_csv, fetch_csv, write_csv, sq_csv=None, commands=""):
-    """Summaries for profiles/: per-kernel durations (kernel-trace stats) and
-    HBM bytes per dispatch from FETCH_SIZE / WRITE_SIZE (KiB), each scaled by what
-    the counter reads for the 1 GiB copies of known size; optionally vector
-    memory / LDS instruction counts and LDS bank conflicts per dispatch."""
+    """Summaries for profiles/: per-kernel durations and HBM bytes per dispatch
+    from FETCH_SIZE / WRITE_SIZE (KiB), each scaled by what the counter reads for
+    the 1 GiB device copies of known size; optionally vector memory / LDS
+    instruction counts and LDS bank conflicts per dispatch.  Dispatches are kept
+    apart by kernel and grid size (one kernel runs at several sizes); durations
+    come from the per-dispatch kernel trace next to `stats_csv`."""
     import csv
     import collections
     import statistics
 
     def norm(name):                               # "void mxq::k<false>(...)" -> "mxq::k<false>"
-        name = name.split("(")[0]
+        name = name.replace("(anonymous namespace)::", "").split("(")[0]
         return name[5:] if name.startswith("void ") else name
 
-    def per_kernel(path, field="Counter_Value"):
+    def per_dispatch_counter(path, counter=None):
         agg = collections.defaultdict(list)
         for r in csv.DictReader(open(path)):
-            agg[norm(r["Kernel_Name"])].append(float(r[field]))
+            if counter is None or r["Counter_Name"] == counter:
+                agg[(norm(r["Kernel_Name"]), int(r["Grid_Size"]))].append(float(r["Counter_Value"]))
         return agg
 
-    fetch, write = per_kernel(fetch_csv), per_kernel(write_csv)
-    f_copy = max(fetch[COPY_KERNEL]) * 1024.0
-    w_copy = max(write[COPY_KERNEL]) * 1024.0
+    fetch, write = per_dispatch_counter(fetch_csv), per_dispatch_counter(write_csv)
+    copies_f = [v for (k, _), vs in fetch.items() if k == COPY_KERNEL for v in vs]
+    copies_w = [v for (k, _), vs in write.items() if k == COPY_KERNEL for v in vs]
+    f_copy, w_copy = max(copies_f) * 1024.0, max(copies_w) * 1024.0      # the 1 GiB copies are the largest
     f_scale, w_scale = COPY_BYTES / f_copy, COPY_BYTES / w_copy
-    stats = {norm(r["Name"]): r for r in csv.DictReader(open(stats_csv))}
-    mxb = mx_bytes(*DISPATCH)
-    algo = {"mxq::mx_quantize_kernel<false>": mxb, "mxq::mx_quantize_kernel<true>": mxb,
-            "mxq::mx_dequantize_kernel": mxb, "mxq::mx_quantize_dim0_kernel<false>": mxb,
-            "mxq::mx_quantize_dim0_kernel<true>": mxb, "mxq::mx_dequantize_dim0_kernel": mxb,
-            "mxq::mx_dispatch_pack_kernel": mxb + 4 * DISPATCH[0],
-            "mxq::transpose_u8_kernel": transpose_bytes(*TOKENS)}
+    n_cal = sum(1 for v in copies_f if v * 1024.0 > 0.99 * f_copy)
+    durations = collections.defaultdict(list)
+    trace_csv = stats_csv.replace("_kernel_stats.csv", "_kernel_trace.csv")
+    for r in csv.DictReader(open(trace_csv)):
+        g = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+        durations[(norm(r["Kernel_Name"]), g)].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+
+    D, T = DISPATCH, TOKENS
+    known = {   # (kernel, grid) -> (workload, algorithmic bytes per dispatch)
+        ("mxq::mx_quantize_kernel<false>", grid_mx(*D)): ("(65536, 5120)", mx_bytes(*D)),
+        ("mxq::mx_quantize_kernel<false>", grid_mx(*T)): ("(16640, 5120)", mx_bytes(*T)),
+        ("mxq::mx_quantize_kernel<true>", grid_mx(*D)): ("(65536, 5120) RCEIL", mx_bytes(*D)),
+        ("mxq::mx_dequantize_kernel", grid_mx(*D)): ("(65536, 5120)", mx_bytes(*D)),
+        ("mxq::mx_dequantize_kernel", grid_mx(*T)): ("(16640, 5120)", mx_bytes(*T)),
+        ("mxq::mx_quantize_dim0_kernel<false>", grid_dim0(*D)): ("(65536, 5120) dim 0", mx_bytes(*D)),
+        ("mxq::mx_quantize_dim0_kernel<true>", grid_dim0(*D)): ("(65536, 5120) dim 0 RCEIL", mx_bytes(*D)),
+        ("mxq::mx_dequantize_dim0_kernel", grid_dim0(*D)): ("(65536, 5120) dim 0", mx_bytes(*D)),
+        ("mxq::mx_dispatch_pack_kernel", D[0] * 256): ("(65536, 5120) top-1", mx_bytes(*D) + 4 * D[0]),
+        ("mxq::transpose_u8_kernel", grid_transpose(T[1], T[0])): ("5120 x 16640", transpose_bytes(*T)),
+    }
+    for G in (16, 32, 64, 128):
+        known[("mxq::group_hold_kernel<0>", grid_hold(*T, G))] = (f"(16640, 5120) G={G} row", None)
+    known[("mxq::group_amax_kernel<1>", grid_hold(*T, 128))] = ("(16640, 5120) G=128 col", None)
+    known[("mxq::group_finalize_kernel", grid_finalize(T[1], 128))] = ("G=128", None)
+    known[("mxq::group_quant_col_blocks_kernel", grid_col_blocks(*T))] = ("(16640, 5120) col", None)
+    known[("mxq::group_split_amax_kernel<256>", grid_split_amax(*T))] = ("(16640, 5120)", None)
+    known[("mxq::group_split_quant_kernel<1>", grid_split_quant(*T))] = ("(16640, 5120) col", None)
+    known[("mxq::group_split_amax_kernel<256>", grid_split_amax(T[0], 8192))] = ("(16640, 8192) dY", None)
+    known[("mxq::group_split_quant_kernel<1>", grid_split_quant(T[0], 8192))] = ("(16640, 8192) dY col", None)
+    known[("mxq::group_split_quant_kernel<0>", grid_split_quant(*T))] = ("(16640, 5120) row, forced", None)
+    known[("mxq::group_amax_kernel<0>", grid_hold(*T, 16))] = ("(16640, 5120) G=16 row, forced", None)
+    known[("mxq::group_quant_kernel<0>", grid_hold(*T, 16))] = ("(16640, 5120) G=16 row, forced", None)
+    known[("mxq::group_finalize_kernel", grid_finalize(T[1], 16))] = ("G=16, forced", None)
+
     lines = ["# HBM traffic per dispatch, hot-path step (dispatch payload 65536x5120, tokens 16640x5120)", "",
              "Commands (from the repository root):", "", "```", commands.strip(), "```", "",
-             f"Calibration: {COPY_KERNEL} copies of 1 GiB read {f_copy / 1024:.1f} KiB by FETCH_SIZE and "
-             f"write {w_copy / 1024:.1f} KiB by WRITE_SIZE; scale factors {f_scale:.4f} (fetch) and "
+             f"Calibration: the {n_cal} {COPY_KERNEL} copies of 1 GiB read {f_copy / 1024:.1f} KiB by FETCH_SIZE "
+             f"and write {w_copy / 1024:.1f} KiB by WRITE_SIZE; scale factors {f_scale:.4f} (fetch) and "
              f"{w_scale:.4f} (write).", "",
-             "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled HBM bytes / dispatch | "
-             "algorithmic bytes | ratio |", "|---|---|---|---|---|---|---|"]
+             "Rows are per kernel and launch grid (work-items); the workload is named where the bench runs that "
+             "kernel at that grid.", "",
+             "| kernel | workload | grid | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled HBM bytes / dispatch | "
+             "algorithmic bytes | ratio | average us (trace) |", "|---|---|---|---|---|---|---|---|---|---|"]
     out = {"source_files": COUNTER_SOURCES, "fetch_scale": f_scale, "write_scale": w_scale, "kernels": {}}
     src_hash = kernel_source_hash(COUNTER_SOURCES)
-    for k in sorted(fetch):
-        if k == COPY_KERNEL or k not in write:
-            continue
-        fk, wk = statistics.mean(fetch[k]), statistics.mean(write[k])
-        hbm = fk * 1024 * f_scale + wk * 1024 * w_scale
-        a = algo.get(k)
-        lines.append(f"| {k} | {len(fetch[k])} | {fk:.1f} | {wk:.1f} | {hbm:,.0f} | "
-                     f"{a if a else '-'} | {hbm / a if a else float('nan'):.4f} |")
-        if a:
-            out["kernels"][k.split("::")[-1]] = {"hbm_bytes_per_launch": round(hbm), "algorithmic_bytes": a,
-                                                 "source_sha256": src_hash}
-    # whole group-scaling calls: the kernels each call launches (the plan kernel
-    # is shared by both calls and counted once per call)
-    def per_dispatch(k):
-        if k not in fetch or k not in write:
+
+    def hbm(key):
+        if key not in fetch or key not in write:
             return None
-        return statistics.mean(fetch[k]) * 1024 * f_scale + statistics.mean(write[k]) * 1024 * w_scale
-    calls = [("group scaling G=16 row-major (plan + hold)", ["mxq::group_plan_kernel<128>", "mxq::group_hold_kernel<0>"],
-              group_bytes(TOKENS[0], TOKENS[1], 16)),
-             ("group scaling G=128 column-major (plan + amax + finalize + quantize)",
-              ["mxq::group_plan_kernel<128>", "mxq::group_amax_kernel<1>", "mxq::group_finalize_kernel",
-               "mxq::group_quant_col_blocks_kernel"], group_bytes(TOKENS[0], TOKENS[1], 128)),
+        return statistics.mean(fetch[key]) * 1024 * f_scale + statistics.mean(write[key]) * 1024 * w_scale
+
+    for key in sorted(fetch):
+        k, grid = key
+        if k == COPY_KERNEL or key not in write:
+            continue
+        what, a = known.get(key, ("", None))
+        h = hbm(key)
+        dur = f"{statistics.mean(durations[key]):.2f}" if durations.get(key) else "-"
+        lines.append(f"| {k} | {what or '-'} | {grid} | {len(fetch[key])} | {statistics.mean(fetch[key]):.1f} | "
+                     f"{statistics.mean(write[key]):.1f} | {h:,.0f} | {a if a else '-'} | "
+                     f"{h / a if a else float('nan'):.4f} | {dur} |")
+        if a and what.startswith("(65536, 5120)"):
+            out["kernels"][k.split("::")[-1]] = {"hbm_bytes_per_launch": round(h), "algorithmic_bytes": a,
+                                                 "source_sha256": src_hash}
+
+    # whole calls: the kernels each call launches at that call's grid (the
+    # plan kernels are shared by several calls and counted at their mean)
+    def any_grid(k):
+        keys = [key for key in fetch if key[0] == k]
+        if not keys or any(key not in write for key in keys):
+            return None
+        return statistics.mean(hbm(key) for key in keys)
+
+    calls = [("group scaling G=16 row-major, hold (plan + hold)",
+              [("mxq::group_plan_kernel<128>", None), ("mxq::group_hold_kernel<0>", grid_hold(*T, 16))],
+              group_bytes(T[0], T[1], 16)),
+             ("group scaling G=128 column-major, two-pass (plan + amax + finalize + quantize)",
+              [("mxq::group_plan_kernel<128>", None), ("mxq::group_amax_kernel<1>", grid_hold(*T, 128)),
+               ("mxq::group_finalize_kernel", grid_finalize(T[1], 128)),
+               ("mxq::group_quant_col_blocks_kernel", grid_col_blocks(*T))], group_bytes(T[0], T[1], 128)),
+             ("group scaling column-major, split (amax + quantize; mean over its calls at 16, 32 and 64 groups)",
+              [("mxq::group_split_amax_kernel<256>", grid_split_amax(*T)),
+               ("mxq::group_split_quant_kernel<1>", grid_split_quant(*T))],
+              sum(group_bytes(T[0], T[1], g) for g in (16, 32, 64)) // 3),
              ("dispatch pack, top-1 over 16 experts (count + place with the scan folded in + pack)",
-              ["mxq::dp_count_kernel", "mxq::dp_place_scan_kernel", "mxq::mx_dispatch_pack_kernel"],
-              mx_bytes(*DISPATCH) + 8 * DISPATCH[0])]
+              [("mxq::dp_count_kernel", None), ("mxq::dp_place_scan_kernel", None),
+               ("mxq::mx_dispatch_pack_kernel", D[0] * 256)], mx_bytes(*D) + 8 * D[0])]
     lines += ["", "Whole calls (sum of the kernels each call launches):", "",
               "| call | scaled HBM bytes | algorithmic bytes | ratio |", "|---|---|---|---|"]
     for name, ks, a in calls:
-        parts = [per_dispatch(k) for k in ks]
+        parts = [any_grid(k) if g is None else hbm((k, g)) for k, g in ks]
         if any(x is None for x in parts):
             continue
         lines.append(f"| {name} | {sum(parts):,.0f} | {a} | {sum(parts) / a:.4f} |")
     if sq_csv:
         sq = collections.defaultdict(lambda: collections.defaultdict(list))
         for r in csv.DictReader(open(sq_csv)):
-            sq[r["Kernel_Name"].split("(")[0]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+            sq[(norm(r["Kernel_Name"]), int(r["Grid_Size"]))][r["Counter_Name"]].append(float(r["Counter_Value"]))
         names = sorted({c for k in sq.values() for c in k})
         lines += ["", "Vector memory, LDS and wave counts per dispatch (means):", "",
-                  "| kernel | " + " | ".join(names) + " |", "|---" * (len(names) + 1) + "|"]
-        for k in sorted(sq):
-            if k == COPY_KERNEL:
+                  "| kernel | grid | " + " | ".join(names) + " |", "|---" * (len(names) + 2) + "|"]
+        for key in sorted(sq):
+            if key[0] == COPY_KERNEL or key[0].startswith("at::"):
                 continue
-            lines.append(f"| {k} | " + " | ".join(f"{statistics.mean(sq[k][c]):,.0f}" if sq[k][c] else "-"
-                                                 for c in names) + " |")
-    lines += ["", "Kernel durations (rocprofv3 --kernel-trace --stats):", "",
+            lines.append(f"| {key[0]} | {key[1]} | " + " | ".join(
+                f"{statistics.mean(sq[key][c]):,.0f}" if sq[key][c] else "-" for c in names) + " |")
+    lines += ["", "Kernel durations (rocprofv3 --kernel-trace --stats, all grids of a kernel together):", "",
               "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
-    for k, r in stats.items():
+    for r in csv.DictReader(open(stats_csv)):
+        k = norm(r["Name"])
+        if k.startswith("at::"):
+            continue
         lines.append(f"| {k} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
                      f"{float(r['MaxNs']) / 1e3:.2f} |")
     os.makedirs(PROFILES, exist_ok=True)
@@ -569,16 +661,16 @@ def main():
         st = launch_stats(torch, stream, fn, reps)
         mx_tokens[name] = {**st, **rate(mx_bytes(M2, K2), st["median_us"]), "shape": [M2, K2]}
     del xq_t, xs_t, y_t
-    # Group scaling (16 groups, row-major) while a streaming copy of 2 GiB runs
+    # Group scaling (16 groups, row-major) while streaming copies of 1 GiB run
     # on a second stream of the same GPU, against the same call alone: the hold
     # method (the default; it keeps a group's tiles resident together, so other
     # work on the device can make its waits run out), with its route counters,
     # and the two methods that never wait, forced through the tuning hook.
     side = torch.cuda.Stream()
-    big_src = torch.empty(1 << 31, dtype=torch.uint8, device=dev)
+    big_src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     big_dst = torch.empty_like(big_src)
     g16 = lambda i: mxq.mxq_group_scale_fp8(sets[i % len(sets)].x2, offs16, ROW, sets[0].q2, sets[0].sc2, ws, stream)
-    concurrency = {"what": ("group scaling (16640, 5120), 16 groups, row-major, while 2 GiB device copies run "
+    concurrency = {"what": ("group scaling (16640, 5120), 16 groups, row-major, while 1 GiB device copies run "
                             "on a second stream; per-launch events on the call's stream")}
     for method in ("hold", "split", "twopass"):
         with mxq.group_scale_knobs(method=method):
@@ -587,8 +679,8 @@ def main():
             alone = launch_stats(torch, stream, g16, 10)
             torch.cuda.synchronize()
             with torch.cuda.stream(side):
-                for _ in range(4):
-                    big_dst.copy_(big_src)                # about 4 x 0.8 ms of copying queued on the side stream
+                for _ in range(8):
+                    big_dst.copy_(big_src)                # about 8 x 0.4 ms of copying queued on the side stream
             beside = launch_stats(torch, stream, g16, 10)     # issued at once, overlapping the copies
             entry = {"alone": alone, "beside_streaming_copy": beside}
             if method == "hold":

@@ -150,6 +150,24 @@ __device__ __forceinline__ void buf_store8(uint2 v, Rsrc r, uint32_t off, uint32
     __builtin_amdgcn_raw_buffer_store_b64(w, r, off, soff, kNonTemporal);
 }
 
+// Workgroup-wide OR of a predicate; every thread of the workgroup must call it.
+// Each wave's ballot goes to its own LDS word, which every lane then reads back
+// as a broadcast; the closing barrier keeps the next vote's writes behind these
+// reads.  (The built-in __syncthreads_or has every lane OR into one LDS word:
+// 64 serialised accesses per wave.)  It is also a full workgroup barrier.
+template <int NWAVES>
+__device__ __forceinline__ bool block_any(bool p, uint32_t* votes)
+{
+    const bool wave_any = __ballot(p) != 0ull;
+    if ((threadIdx.x & 63) == 0) votes[threadIdx.x >> 6] = wave_any ? 1u : 0u;
+    __syncthreads();
+    uint32_t r = 0;
+#pragma unroll
+    for (int i = 0; i < NWAVES; ++i) r |= votes[i];
+    __syncthreads();
+    return r != 0u;
+}
+
 // An opaque copy: the compiler cannot relate the result to its input, so
 // offsets derived from it are recomputed where used instead of being kept in
 // registers from an earlier phase.

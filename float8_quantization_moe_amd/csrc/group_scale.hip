@@ -438,7 +438,11 @@ struct TileShared {
     // (the column-layout staging tile only where a kernel stores q)
     __align__(16) uint8_t stage[LAYOUT == 1 && STAGE ? TileCfg<LAYOUT>::W * TileCfg<LAYOUT>::R : 16];
     uint4 red[TileCfg<LAYOUT>::NS][TileCfg<LAYOUT>::CG];
-    __align__(16) float scale[TileCfg<LAYOUT>::W];
+    // a lane's 8 scales as two float4 indexed by its column group, so that a
+    // wave reads 1 KB of consecutive LDS (a 32-byte lane stride put 64 lanes on
+    // 8 banks)
+    float4 scale_lo[TileCfg<LAYOUT>::CG], scale_hi[TileCfg<LAYOUT>::CG];
+    __align__(16) uint32_t vote[TileCfg<LAYOUT>::T / 64];
     int state;
 };
 
@@ -525,8 +529,8 @@ __device__ __forceinline__ void finish_strip(uint4 a, const TileInfo& t, int K, 
     if (rs == 0) {
         max_rows(a, &sh.red[0][cg], C::NS, C::CG);
         const float4 lo = scales_lo(a, ws.pow2), hi = scales_hi(a, ws.pow2);
-        *(float4*)(sh.scale + cg * 8) = lo;
-        *(float4*)(sh.scale + cg * 8 + 4) = hi;
+        sh.scale_lo[cg] = lo;
+        sh.scale_hi[cg] = hi;
         if (k < K) {
             float* dst = scales + (int64_t)t.g * K + k;
             if (publish) {
@@ -543,7 +547,7 @@ __device__ __forceinline__ void finish_strip(uint4 a, const TileInfo& t, int K, 
         }
     }
     __syncthreads();
-    cs = make_col_scales(*(const float4*)(sh.scale + cg * 8), *(const float4*)(sh.scale + cg * 8 + 4));
+    cs = make_col_scales(sh.scale_lo[cg], sh.scale_hi[cg]);
 }
 
 // The strip's column maxima over all of the group's rows, read from the input
@@ -610,7 +614,7 @@ __device__ __forceinline__ void reduce_strip(const uint16_t* __restrict__ x, con
             }
         }
     }
-    if (__syncthreads_or(!ok)) a = strip_max_fallback<LAYOUT>(x, t, K, k, rs, ws);   // a partial never came
+    if (block_any<C::T / 64>(!ok, sh.vote)) a = strip_max_fallback<LAYOUT>(x, t, K, k, rs, ws);   // a partial never came
     finish_strip<LAYOUT>(a, t, K, k, cg, rs, ws, scales, scales_coherent, sh, cs);
 }
 
@@ -638,10 +642,10 @@ __device__ __forceinline__ bool wait_scales(const float* __restrict__ scales, co
                 }
             }
         }
-        *(float4*)(sh.scale + cg * 8) = bits_f4(s0);
-        *(float4*)(sh.scale + cg * 8 + 4) = bits_f4(s1);
+        sh.scale_lo[cg] = bits_f4(s0);
+        sh.scale_hi[cg] = bits_f4(s1);
     }
-    return !__syncthreads_or(!ok);
+    return !block_any<sizeof(Sh::vote) / sizeof(uint32_t)>(!ok, sh.vote);
 }
 
 // Chunk `jc`'s partial row, computed from the input and published (agent
@@ -654,7 +658,7 @@ __device__ __forceinline__ void publish_chunk_if_missing(const uint16_t* __restr
     using C = TileCfg<LAYOUT>;
     uint16_t* dst = ws.partial + (int64_t)jc * K + k;
     const bool missing = rs == 0 && k < K && !partial_written(load_coherent(dst));
-    if (!__syncthreads_or(missing)) return;
+    if (!block_any<C::T / 64>(missing, sh.vote)) return;
     const int4 e = *(const int4*)(ws.table + jc);         // group, rows [r0, r1) (at most R), first chunk
     uint4 m = make_uint4(0, 0, 0, 0);
     if (k < K) {
@@ -760,9 +764,9 @@ void group_hold_kernel(const uint16_t* __restrict__ x, int M, int K, int G, int 
                 finish_strip<LAYOUT>(strip_max_fallback<LAYOUT>(x, t, K, k, rs, ws), t, K, k, cg, rs, ws, scales, true,
                                      sh, cs);
             else
-                cs = make_col_scales(*(const float4*)(sh.scale + cg * 8), *(const float4*)(sh.scale + cg * 8 + 4));
+                cs = make_col_scales(sh.scale_lo[cg], sh.scale_hi[cg]);
         } else {
-            cs = make_col_scales(*(const float4*)(sh.scale + cg * 8), *(const float4*)(sh.scale + cg * 8 + 4));
+            cs = make_col_scales(sh.scale_lo[cg], sh.scale_hi[cg]);
         }
     }
     quantize_store_tile<LAYOUT>(v, cs, t, M, K, k, cg, rs, q, sh.stage, false);

@@ -45,10 +45,10 @@ constexpr int CG = kSW / 8;           // lanes per row (8 columns each)
 constexpr int NS = kST / CG;          // row slots
 constexpr int H = kSR / NS;           // consecutive rows per lane
 constexpr int kWaves = kST / 64;
-#ifndef MXQ_SPLIT_AMAX_WIDTH
-#define MXQ_SPLIT_AMAX_WIDTH 256
-#endif
-constexpr int kSplitAmaxWidth = MXQ_SPLIT_AMAX_WIDTH;   // amax-pass tile width (columns)
+// Amax-pass tile width (columns).  Measured at 16640 x 5120, column-major (amax
+// pass alone, kernel trace): 128 / 256 / 512 columns take 30.3 / 29.7 / 30.9 us
+// at 16 groups and 35.7 / 36.8 / 39.2 us at 128 groups.
+constexpr int kSplitAmaxWidth = 256;
 static_assert(H == 8 && CG == 16, "tile shape");
 
 // Inclusive running maximum over the lanes of a wave (values >= 0): DPP row
@@ -138,7 +138,8 @@ struct SplitShared {
         __align__(16) uint8_t stage[kSW * kSR];          // column-major staging (quantize pass, at the end)
         uint4 red[kWaves][CG];                           // per-wave column maxima (before that)
     };
-    __align__(16) float scale[kSW];
+    float4 scale_lo[CG], scale_hi[CG];                   // a lane's 8 scales, by column group
+    __align__(16) uint32_t vote[kWaves];
 };
 
 // Column maxima over the row slots: the 4 row slots of a wave first (lanes 16
@@ -292,8 +293,8 @@ void group_split_quant_kernel(const uint16_t* __restrict__ x, int M, int K, cons
         a = reduce_slots(a, cg, sh);
         if (rs == 0) {
             const float4 lo4 = scales_lo(a, pow2), hi4 = scales_hi(a, pow2);
-            *(float4*)(sh.scale + cg * 8) = lo4;
-            *(float4*)(sh.scale + cg * 8 + 4) = hi4;
+            sh.scale_lo[cg] = lo4;
+            sh.scale_hi[cg] = hi4;
             if (blk == fb && k < K) {                     // the group's first block stores its scales
                 float* dst = scales_out + (int64_t)g * K + k;
                 *(float4*)dst = inverse ? inverse4(lo4) : lo4;
@@ -301,8 +302,8 @@ void group_split_quant_kernel(const uint16_t* __restrict__ x, int M, int K, cons
             }
         }
         __syncthreads();
-        const ColScales cs = make_col_scales(*(const float4*)(sh.scale + cg * 8), *(const float4*)(sh.scale + cg * 8 + 4));
-        const bool fix = __syncthreads_or((cs.nan_lo | cs.nan_hi) != 0u);   // (also: sh.scale free again)
+        const ColScales cs = make_col_scales(sh.scale_lo[cg], sh.scale_hi[cg]);
+        const bool fix = block_any<kWaves>((cs.nan_lo | cs.nan_hi) != 0u, sh.vote);   // (also: the scales in LDS free again)
         const uint32_t sh16 = opaque_u32(16u), mhi = opaque_u32(0xFFFF0000u);
         if (lo <= rbase && hi >= rbase + H) {             // all the lane's rows in this group
 #pragma unroll
