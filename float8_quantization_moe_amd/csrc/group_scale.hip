@@ -20,7 +20,7 @@
 //          strip) arrival counters and per-tile "deferred" marks, and fill the
 //          partial maxima and the scales with values no result takes ("not yet
 //          written").
-//   hold   one workgroup per tile (a 128-row chunk of one group x 512 columns).
+//   hold   one workgroup per tile (a 128-row chunk of one group x 256 columns).
 //          It loads its tile into registers, reduces the column maxima (packed
 //          16-bit max of |bf16 bits| -- positive bf16 order is integer order and
 //          Inf/NaN sort above every finite value), publishes them as one row of
@@ -49,12 +49,15 @@
 // Row chunks never cross a group boundary and are cut at multiples of the tile
 // height, so interior tiles are aligned in both output layouts.  The plan kernel
 // writes one table entry per chunk (group, rows, the group's chunk range), so a
-// tile learns where it is with one load.  Tiles are 128 rows x 512 columns for
-// 512 threads; each lane holds 8 columns of 16 rows.  Row layout: rows 8 apart
-// per lane, a wave writes 512 contiguous bytes of one row.  Column layout: 16
-// consecutive rows per lane, turned into dwords of 4 consecutive rows per
-// column, staged as a 512 x 128-byte transposed tile in LDS, written as 128
-// contiguous bytes per output row.
+// tile learns where it is with one load.  Tiles are 128 rows x 256 columns for
+// 256 threads; each lane holds 8 columns of 16 rows.  (128 x 512 tiles for 512
+// threads took 67 / 69 / 71 / 78 us at 16 / 32 / 64 / 128 groups, row-major,
+// 16640 x 5120, against 65 / 66 / 68 / 73 us; 128 x 128 tiles for 128 threads
+// matched the 256-column ones; column-major at 16 groups 78 against 74 us.)
+// Row layout: rows 8 apart per lane, a wave writes 256 contiguous bytes of each
+// of two rows.  Column layout: 16 consecutive rows per lane, turned into dwords
+// of 4 consecutive rows per column, staged as a 256 x 128-byte transposed tile
+// in LDS, written as 128 contiguous bytes per output row.
 #include <atomic>
 #include <mutex>
 
@@ -68,7 +71,7 @@ template <int LAYOUT>
 struct TileCfg;
 template <>
 struct TileCfg<0> {                 // row-major output
-    static constexpr int T = 512, H = 16, W = 512;
+    static constexpr int T = 256, H = 16, W = 256;
     static constexpr int CG = W / 8;                  // 8-column groups per strip (lanes per row)
     static constexpr int NS = T / CG;                 // lanes sharing the same columns
     static constexpr int R = NS * H;
@@ -76,7 +79,7 @@ struct TileCfg<0> {                 // row-major output
 };
 template <>
 struct TileCfg<1> {                 // column-major output
-    static constexpr int T = 512, H = 16, W = 512;
+    static constexpr int T = 256, H = 16, W = 256;
     static constexpr int CG = W / 8;
     static constexpr int NS = T / CG;
     static constexpr int R = NS * H;
@@ -1088,16 +1091,18 @@ static hipError_t launch_layout(const void* x, int M, int K, const int32_t* offs
     // claimant reads the group's rows of the strip, one workgroup alone)
     const unsigned long long rescue_ticks = ticks_per_ms * 50ull;
     // The method.  Default, from measurements at 16640 x 5120 (16 to 128 Zipf
-    // groups): row-major output holds (one read of X; 70-82 us against 74-103 us
-    // for either two-pass method).  Column-major output splits into two
-    // streaming passes while the average group spans at least two 128-row
-    // blocks (76-86 us against 81-105 us: the hold kernel's tiles, cut at group
-    // boundaries, split output lines, and the four-launch two-pass method pays
-    // two more kernel boundaries), and takes the four-launch two-pass method with
-    // more groups (90 us against 106 us: the split method's quantize pass then
-    // reduces several groups per block).
-    bool twopass = LAYOUT == 1 && 5 * (int64_t)G >= (M + 127) / 128;
-    bool split = LAYOUT == 1 && 2 * (int64_t)G <= (M + 127) / 128 && group_split_sizes_ok(M, K, G);
+    // groups): row-major output holds (one read of X; 65-73 us against 75-100 us
+    // for the two-read methods).  Column-major output holds while the average
+    // group spans at least eight 128-row blocks (74 against 76 us at 16 groups),
+    // splits into two streaming passes while it spans at least two (78-84 us
+    // against 84-93 us held: the hold kernel's tiles, cut at group boundaries,
+    // split output lines, and the four-launch two-pass method pays two more
+    // kernel boundaries), and takes the four-launch two-pass method with more
+    // groups (88-91 us against 101 us split and 110 us held: the split method's
+    // quantize pass then reduces several groups per block).
+    const int64_t nblk = (M + 127) / 128;
+    bool twopass = LAYOUT == 1 && 5 * (int64_t)G >= nblk;
+    bool split = LAYOUT == 1 && 2 * (int64_t)G <= nblk && 8 * (int64_t)G > nblk && group_split_sizes_ok(M, K, G);
     if (kn.method == 1) twopass = split = false;
     if (kn.method == 2) twopass = true, split = false;
     if (kn.method == 3) split = group_split_sizes_ok(M, K, G);
