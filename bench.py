@@ -83,7 +83,10 @@ def parse_args():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--rotate", type=int, default=4, help="independent buffer sets cycled through")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--no-gemm", action="store_true", help="skip the grouped GEMM leg")
+    p.add_argument("--no-gemm", action="store_true", help="skip the grouped GEMM leg (same as leaving gemm out of --legs)")
+    p.add_argument("--legs", default=",".join(LEGS),
+                   help="comma-separated measurement legs run beside the timed step: " + ", ".join(LEGS))
+    p.add_argument("--seed", type=int, default=0, help="offset added to the seed of every synthetic input")
     p.add_argument("--cpu-mx-rows", type=int, default=49152, help="dispatch rows in the CPU sample")
     p.add_argument("--cpu-group-rows", type=int, default=16640, help="token rows in the CPU sample")
     p.add_argument("--ingest-counters", nargs="+", metavar="CSV",
@@ -94,6 +97,10 @@ def parse_args():
 
 
 COUNTER_SOURCES = ["mx_codec.hip", "mx_dim0.hip", "device_common.hpp"]
+# Legs beside the step: NEXT-row variants, the group-scaling sweep over 16-128
+# groups, the MX codec at the token shape, group scaling beside streaming copies,
+# and the grouped GEMM.
+LEGS = ("variants", "sweep", "tokens", "concurrency", "gemm")
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 COPY_BYTES = 1 << 30       # the 1 GiB device copies of the streaming-ceiling leg
 
@@ -351,7 +358,7 @@ def bench_grouped_mm(args, dev, stream, x_host, ends, W, mxq, np, torch):
     G, N, K = EXPERTS
     M = x_host.shape[0]
     offs = torch.from_numpy(ends).to(dev)
-    w_host = W.expert_weights(G, N, K, seed=2)
+    w_host = W.expert_weights(G, N, K, seed=2 + args.seed)
     w_dev = w_host.to(dev).view(G * N, K)
     del w_host
     wq = torch.empty((G * N, K), dtype=torch.uint8, device=dev)
@@ -397,7 +404,7 @@ def bench_grouped_mm(args, dev, stream, x_host, ends, W, mxq, np, torch):
     # the same product on the packed dispatch payload (tokens routed top-1 by the
     # Zipf draw whose group sizes these are), packed by mxq_dispatch_pack_mx
     x_dev = x_host.to(dev)
-    ids = torch.from_numpy(W.routed_expert_ids(M, G, topk=1, seed=1)).to(dev)
+    ids = torch.from_numpy(W.routed_expert_ids(M, G, topk=1, seed=1 + args.seed)).to(dev)
     packed = torch.empty((M, K + K // 32), dtype=torch.uint8, device=dev)
     pends = torch.empty(G, dtype=torch.int32, device=dev)
     src = torch.empty(M, dtype=torch.int32, device=dev)
@@ -449,8 +456,14 @@ def main():
     if args.gpus != 1 or world != 1:
         print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} (WORLD_SIZE={world}) is not "
               "supported.  The quantization kernels shard by token rows with no exchange of their own; "
-              "see the design notes for how the all-to-all would carry the buffers.", file=sys.stderr)
+              "the all-to-all that would carry their buffers between GPUs is not part of this path.", file=sys.stderr)
         sys.exit(2)
+    legs = {l.strip() for l in args.legs.split(",") if l.strip()}
+    unknown = legs - set(LEGS)
+    if unknown:
+        raise SystemExit(f"--legs: unknown {sorted(unknown)}; choose from {', '.join(LEGS)}")
+    if args.no_gemm:
+        legs.discard("gemm")
 
     import numpy as np
     import torch
@@ -466,10 +479,10 @@ def main():
     # ------------------------------------------------------ synthetic inputs --
     M1, K1 = DISPATCH
     M2, K2 = TOKENS
-    x1_host = W.dispatch_payload(M1, K1, seed=0)
-    x2_host = W.moe_tokens(M2, K2, seed=0)
-    ends16 = W.zipf_group_ends(M2, G_ROW, seed=1)
-    ends128 = W.zipf_group_ends(M2, G_COL, seed=1)
+    x1_host = W.dispatch_payload(M1, K1, seed=args.seed)
+    x2_host = W.moe_tokens(M2, K2, seed=args.seed)
+    ends16 = W.zipf_group_ends(M2, G_ROW, seed=1 + args.seed)
+    ends128 = W.zipf_group_ends(M2, G_COL, seed=1 + args.seed)
     x1_dev = x1_host.to(dev)
     x2_dev = x2_host.to(dev)
     offs16 = torch.from_numpy(ends16).to(dev)
@@ -547,148 +560,156 @@ def main():
         per_call_us[c] = e0.elapsed_time(e1) * 1e3 / reps
     per_call_dist = {c: launch_stats(torch, stream, lambda r, j=j: fns_per_set[r % len(sets)][j](), reps)
                      for j, c in enumerate(calls)}
-    # Variants of the path's calls (the NEXT rows), each alone on the same rotated
-    # buffers and shapes; reported beside the step, not part of `value`.
-    FLOOR, RCEIL = mxq.MXQ_SCALE_FLOOR, mxq.MXQ_SCALE_RCEIL
-    POW2, INV = mxq.MXQ_GROUP_POW2_SCALE, mxq.MXQ_GROUP_INVERSE_SCALE
-    s_dim0 = lambda b: b.s1.view(M1 // 32, K1)      # (M/32, K) scales: the same byte count as (M, K/32)
-    variant_calls = [
-        ("mx_quantize_rows_rceil", mx_bytes(M1, K1), lambda b: mxq.mxq_quantize_mx_ex(b.x1, 1, RCEIL, b.q1, b.s1, stream)),
-        ("mx_quantize_cols_floor", mx_bytes(M1, K1), lambda b: mxq.mxq_quantize_mx_ex(b.x1, 0, FLOOR, b.q1, s_dim0(b), stream)),
-        ("mx_quantize_cols_rceil", mx_bytes(M1, K1), lambda b: mxq.mxq_quantize_mx_ex(b.x1, 0, RCEIL, b.q1, s_dim0(b), stream)),
-        ("mx_dequantize_cols", mx_bytes(M1, K1), lambda b: mxq.mxq_dequantize_mx_ex(b.q1, s_dim0(b), 0, b.y1, stream)),
-        ("group_scale_g16_row_pow2_inverse", group_bytes(M2, K2, G_ROW),
-         lambda b: mxq.mxq_group_scale_fp8_ex(b.x2, offs16, ROW, POW2 | INV, b.q2, b.sc2, ws, stream)),
-        ("group_scale_g128_col_pow2_inverse", group_bytes(M2, K2, G_COL),
-         lambda b: mxq.mxq_group_scale_fp8_ex(b.x3, offs128, COL, POW2 | INV, b.q3, b.sc3, ws, stream)),
-    ]
     variants = {}
-    for name, nbytes, fn in variant_calls:
-        for b in sets:
-            fn(b)
+    if "variants" in legs:
+        # Variants of the path's calls (the NEXT rows), each alone on the same rotated
+        # buffers and shapes; reported beside the step, not part of `value`.
+        FLOOR, RCEIL = mxq.MXQ_SCALE_FLOOR, mxq.MXQ_SCALE_RCEIL
+        POW2, INV = mxq.MXQ_GROUP_POW2_SCALE, mxq.MXQ_GROUP_INVERSE_SCALE
+        s_dim0 = lambda b: b.s1.view(M1 // 32, K1)      # (M/32, K) scales: the same byte count as (M, K/32)
+        variant_calls = [
+            ("mx_quantize_rows_rceil", mx_bytes(M1, K1), lambda b: mxq.mxq_quantize_mx_ex(b.x1, 1, RCEIL, b.q1, b.s1, stream)),
+            ("mx_quantize_cols_floor", mx_bytes(M1, K1), lambda b: mxq.mxq_quantize_mx_ex(b.x1, 0, FLOOR, b.q1, s_dim0(b), stream)),
+            ("mx_quantize_cols_rceil", mx_bytes(M1, K1), lambda b: mxq.mxq_quantize_mx_ex(b.x1, 0, RCEIL, b.q1, s_dim0(b), stream)),
+            ("mx_dequantize_cols", mx_bytes(M1, K1), lambda b: mxq.mxq_dequantize_mx_ex(b.q1, s_dim0(b), 0, b.y1, stream)),
+            ("group_scale_g16_row_pow2_inverse", group_bytes(M2, K2, G_ROW),
+             lambda b: mxq.mxq_group_scale_fp8_ex(b.x2, offs16, ROW, POW2 | INV, b.q2, b.sc2, ws, stream)),
+            ("group_scale_g128_col_pow2_inverse", group_bytes(M2, K2, G_COL),
+             lambda b: mxq.mxq_group_scale_fp8_ex(b.x3, offs128, COL, POW2 | INV, b.q3, b.sc3, ws, stream)),
+        ]
+        variants = {}
+        for name, nbytes, fn in variant_calls:
+            for b in sets:
+                fn(b)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for r in range(reps):
+                fn(sets[r % len(sets)])
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / reps
+            variants[name] = {"avg_us": round(us, 2), "algorithmic_bytes": nbytes, "GBps": round(nbytes / (us * 1e3), 1),
+                              "frac_of_peak": round(nbytes / (us * 1e3) / HBM_PEAK_GBPS, 4),
+                              "shape": [M1, K1] if name.startswith("mx_") else [M2, K2]}
+        # the fused dispatch pack at the dispatch shape: (65536, 5120) routed top-1 over 16 Zipf experts
+        ids1 = torch.from_numpy(W.routed_expert_ids(M1, G_ROW, topk=1, seed=1 + args.seed)).to(dev)
+        pk1 = torch.empty((M1, K1 + K1 // 32), dtype=torch.uint8, device=dev)
+        pe1 = torch.empty(G_ROW, dtype=torch.int32, device=dev)
+        ps1 = torch.empty(M1, dtype=torch.int32, device=dev)
+        pw1 = torch.empty(mxq.mxq_dispatch_pack_workspace_bytes(M1, K1, 1, G_ROW), dtype=torch.uint8, device=dev)
+        fn = lambda i: mxq.mxq_dispatch_pack_mx(sets[i % len(sets)].x1, ids1, G_ROW, pk1, pe1, ps1, pw1, stream)
+        for i in range(2):
+            fn(i)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for r in range(reps):
-            fn(sets[r % len(sets)])
+            fn(r)
         e1.record(stream)
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / reps
-        variants[name] = {"avg_us": round(us, 2), "algorithmic_bytes": nbytes, "GBps": round(nbytes / (us * 1e3), 1),
-                          "frac_of_peak": round(nbytes / (us * 1e3) / HBM_PEAK_GBPS, 4),
-                          "shape": [M1, K1] if name.startswith("mx_") else [M2, K2]}
-    # the fused dispatch pack at the dispatch shape: (65536, 5120) routed top-1 over 16 Zipf experts
-    ids1 = torch.from_numpy(W.routed_expert_ids(M1, G_ROW, topk=1, seed=1)).to(dev)
-    pk1 = torch.empty((M1, K1 + K1 // 32), dtype=torch.uint8, device=dev)
-    pe1 = torch.empty(G_ROW, dtype=torch.int32, device=dev)
-    ps1 = torch.empty(M1, dtype=torch.int32, device=dev)
-    pw1 = torch.empty(mxq.mxq_dispatch_pack_workspace_bytes(M1, K1, 1, G_ROW), dtype=torch.uint8, device=dev)
-    fn = lambda i: mxq.mxq_dispatch_pack_mx(sets[i % len(sets)].x1, ids1, G_ROW, pk1, pe1, ps1, pw1, stream)
-    for i in range(2):
-        fn(i)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for r in range(reps):
-        fn(r)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / reps
-    nb = mx_bytes(M1, K1) + M1 * 4 * 2               # + the ids read and the source indices written
-    variants["dispatch_pack_top1_e16"] = {"avg_us": round(us, 2), "algorithmic_bytes": nb,
-                                          "GBps": round(nb / (us * 1e3), 1),
-                                          "frac_of_peak": round(nb / (us * 1e3) / HBM_PEAK_GBPS, 4),
-                                          "shape": [M1, K1], "what": "sort by expert + gather + MX quantize + pack"}
-    del ids1, pk1, pe1, ps1, pw1
-    # the other operand of the weight-gradient GEMM: dY (16640, 8192), 16 groups, column-major
-    dy = [torch.empty((M2, WGRAD_N), dtype=torch.bfloat16, device=dev).normal_() for _ in range(min(2, len(sets)))]
-    qdy = torch.empty((WGRAD_N, M2), dtype=torch.uint8, device=dev)
-    sdy = torch.empty((G_ROW, WGRAD_N), dtype=torch.float32, device=dev)
-    wsdy = torch.empty(mxq.mxq_group_scale_workspace_bytes(M2, WGRAD_N, G_ROW), dtype=torch.uint8, device=dev)
-    fn = lambda i: mxq.mxq_group_scale_fp8(dy[i % len(dy)], offs16, COL, qdy, sdy, wsdy, stream)
-    for i in range(2):
-        fn(i)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for r in range(reps):
-        fn(r)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / reps
-    nb = group_bytes(M2, WGRAD_N, G_ROW)
-    variants["group_scale_wgrad_dy_g16_col"] = {"avg_us": round(us, 2), "algorithmic_bytes": nb,
-                                                "GBps": round(nb / (us * 1e3), 1),
-                                                "frac_of_peak": round(nb / (us * 1e3) / HBM_PEAK_GBPS, 4),
-                                                "shape": [M2, WGRAD_N]}
-    del dy, qdy, sdy, wsdy
-    # ---------------------------------------------- (16640, 5120) sweeps ---
-    # Per-group scaling over the pages' sweep (16 to 128 groups) in both layouts,
-    # and the column-major route followed by the transform back, timed as one
-    # unit (its bytes: the method's; the transform's are overhead).  Each call
-    # bracketed by its own events; medians reported.
+        nb = mx_bytes(M1, K1) + M1 * 4 * 2               # + the ids read and the source indices written
+        variants["dispatch_pack_top1_e16"] = {"avg_us": round(us, 2), "algorithmic_bytes": nb,
+                                              "GBps": round(nb / (us * 1e3), 1),
+                                              "frac_of_peak": round(nb / (us * 1e3) / HBM_PEAK_GBPS, 4),
+                                              "shape": [M1, K1], "what": "sort by expert + gather + MX quantize + pack"}
+        del ids1, pk1, pe1, ps1, pw1
+        # the other operand of the weight-gradient GEMM: dY (16640, 8192), 16 groups, column-major
+        dy = [torch.empty((M2, WGRAD_N), dtype=torch.bfloat16, device=dev).normal_() for _ in range(min(2, len(sets)))]
+        qdy = torch.empty((WGRAD_N, M2), dtype=torch.uint8, device=dev)
+        sdy = torch.empty((G_ROW, WGRAD_N), dtype=torch.float32, device=dev)
+        wsdy = torch.empty(mxq.mxq_group_scale_workspace_bytes(M2, WGRAD_N, G_ROW), dtype=torch.uint8, device=dev)
+        fn = lambda i: mxq.mxq_group_scale_fp8(dy[i % len(dy)], offs16, COL, qdy, sdy, wsdy, stream)
+        for i in range(2):
+            fn(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for r in range(reps):
+            fn(r)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        nb = group_bytes(M2, WGRAD_N, G_ROW)
+        variants["group_scale_wgrad_dy_g16_col"] = {"avg_us": round(us, 2), "algorithmic_bytes": nb,
+                                                    "GBps": round(nb / (us * 1e3), 1),
+                                                    "frac_of_peak": round(nb / (us * 1e3) / HBM_PEAK_GBPS, 4),
+                                                    "shape": [M2, WGRAD_N]}
+        del dy, qdy, sdy, wsdy
     group_sweep = {}
-    qsets = [torch.empty((M2, K2), dtype=torch.uint8, device=dev) for _ in range(2)]
-    qt = torch.empty((M2, K2), dtype=torch.uint8, device=dev)
-    for G in (16, 32, 64, 128):
-        offs = torch.from_numpy(W.zipf_group_ends(M2, G, seed=1)).to(dev)
-        sc = torch.empty((G, K2), dtype=torch.float32, device=dev)
-        wsg = torch.empty(mxq.mxq_group_scale_workspace_bytes(M2, K2, G), dtype=torch.uint8, device=dev)
-        nb = group_bytes(M2, K2, G)
-        fns = {
-            "row": lambda i: mxq.mxq_group_scale_fp8(sets[i % len(sets)].x2, offs, ROW, qsets[i % 2], sc, wsg, stream),
-            "col": lambda i: mxq.mxq_group_scale_fp8(sets[i % len(sets)].x2, offs, COL, qsets[i % 2], sc, wsg, stream),
-            "col_then_transform_to_row": lambda i: (
-                mxq.mxq_group_scale_fp8(sets[i % len(sets)].x2, offs, COL, qsets[i % 2], sc, wsg, stream),
-                mxq.mxq_transpose_u8(qsets[i % 2].view(K2, M2), qt, stream)),
-        }
-        for name, fn in fns.items():
+    if "sweep" in legs:
+        # ---------------------------------------------- (16640, 5120) sweeps ---
+        # Per-group scaling over the pages' sweep (16 to 128 groups) in both layouts,
+        # and the column-major route followed by the transform back, timed as one
+        # unit (its bytes: the method's; the transform's are overhead).  Each call
+        # bracketed by its own events; medians reported.
+        group_sweep = {}
+        qsets = [torch.empty((M2, K2), dtype=torch.uint8, device=dev) for _ in range(2)]
+        qt = torch.empty((M2, K2), dtype=torch.uint8, device=dev)
+        for G in (16, 32, 64, 128):
+            offs = torch.from_numpy(W.zipf_group_ends(M2, G, seed=1 + args.seed)).to(dev)
+            sc = torch.empty((G, K2), dtype=torch.float32, device=dev)
+            wsg = torch.empty(mxq.mxq_group_scale_workspace_bytes(M2, K2, G), dtype=torch.uint8, device=dev)
+            nb = group_bytes(M2, K2, G)
+            fns = {
+                "row": lambda i: mxq.mxq_group_scale_fp8(sets[i % len(sets)].x2, offs, ROW, qsets[i % 2], sc, wsg, stream),
+                "col": lambda i: mxq.mxq_group_scale_fp8(sets[i % len(sets)].x2, offs, COL, qsets[i % 2], sc, wsg, stream),
+                "col_then_transform_to_row": lambda i: (
+                    mxq.mxq_group_scale_fp8(sets[i % len(sets)].x2, offs, COL, qsets[i % 2], sc, wsg, stream),
+                    mxq.mxq_transpose_u8(qsets[i % 2].view(K2, M2), qt, stream)),
+            }
+            for name, fn in fns.items():
+                for i in range(2):
+                    fn(i)
+                st = launch_stats(torch, stream, fn, reps)
+                group_sweep[f"g{G}_{name}"] = {**st, **rate(nb, st["median_us"])}
+            del offs, sc, wsg
+        del qsets, qt
+    mx_tokens = {}
+    if "tokens" in legs:
+        # MX quantize / dequantize at the token shape (the target names both shapes)
+        xq_t = torch.empty((M2, K2), dtype=torch.uint8, device=dev)
+        xs_t = torch.empty((M2, K2 // 32), dtype=torch.uint8, device=dev)
+        y_t = torch.empty((M2, K2), dtype=torch.bfloat16, device=dev)
+        mx_tokens = {}
+        for name, fn in (("mx_quantize", lambda i: mxq.mxq_quantize_mx(sets[i % len(sets)].x2, xq_t, xs_t, stream)),
+                         ("mx_dequantize", lambda i: mxq.mxq_dequantize_mx(xq_t, xs_t, y_t, stream))):
             for i in range(2):
                 fn(i)
             st = launch_stats(torch, stream, fn, reps)
-            group_sweep[f"g{G}_{name}"] = {**st, **rate(nb, st["median_us"])}
-        del offs, sc, wsg
-    del qsets, qt
-    # MX quantize / dequantize at the token shape (the target names both shapes)
-    xq_t = torch.empty((M2, K2), dtype=torch.uint8, device=dev)
-    xs_t = torch.empty((M2, K2 // 32), dtype=torch.uint8, device=dev)
-    y_t = torch.empty((M2, K2), dtype=torch.bfloat16, device=dev)
-    mx_tokens = {}
-    for name, fn in (("mx_quantize", lambda i: mxq.mxq_quantize_mx(sets[i % len(sets)].x2, xq_t, xs_t, stream)),
-                     ("mx_dequantize", lambda i: mxq.mxq_dequantize_mx(xq_t, xs_t, y_t, stream))):
-        for i in range(2):
-            fn(i)
-        st = launch_stats(torch, stream, fn, reps)
-        mx_tokens[name] = {**st, **rate(mx_bytes(M2, K2), st["median_us"]), "shape": [M2, K2]}
-    del xq_t, xs_t, y_t
-    # Group scaling (16 groups, row-major) while streaming copies of 1 GiB run
-    # on a second stream of the same GPU, against the same call alone: the hold
-    # method (the default; it keeps a group's tiles resident together, so other
-    # work on the device can make its waits run out), with its route counters,
-    # and the two methods that never wait, forced through the tuning hook.
-    side = torch.cuda.Stream()
-    big_src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-    big_dst = torch.empty_like(big_src)
-    g16 = lambda i: mxq.mxq_group_scale_fp8(sets[i % len(sets)].x2, offs16, ROW, sets[0].q2, sets[0].sc2, ws, stream)
-    concurrency = {"what": ("group scaling (16640, 5120), 16 groups, row-major, while 1 GiB device copies run "
-                            "on a second stream; per-launch events on the call's stream")}
-    for method in ("hold", "split", "twopass"):
-        with mxq.group_scale_knobs(method=method):
-            for i in range(2):
-                g16(i)
-            alone = launch_stats(torch, stream, g16, 10)
-            torch.cuda.synchronize()
-            with torch.cuda.stream(side):
-                for _ in range(8):
-                    big_dst.copy_(big_src)                # about 8 x 0.4 ms of copying queued on the side stream
-            beside = launch_stats(torch, stream, g16, 10)     # issued at once, overlapping the copies
-            entry = {"alone": alone, "beside_streaming_copy": beside}
-            if method == "hold":
-                t_out, reread = mxq.mxq_group_scale_route_counters(ws, M2, K2, len(ends16), ROW, stream)
-                entry["last_call_route_counters"] = {"timed_out_tiles": t_out, "tiles_reread_from_x": reread}
-            torch.cuda.synchronize()
-        concurrency[method] = entry
-    del big_src, big_dst, side
+            mx_tokens[name] = {**st, **rate(mx_bytes(M2, K2), st["median_us"]), "shape": [M2, K2]}
+        del xq_t, xs_t, y_t
+    concurrency = {}
+    if "concurrency" in legs:
+        # Group scaling (16 groups, row-major) while streaming copies of 1 GiB run
+        # on a second stream of the same GPU, against the same call alone: the hold
+        # method (the default; it keeps a group's tiles resident together, so other
+        # work on the device can make its waits run out), with its route counters,
+        # and the two methods that never wait, forced through the tuning hook.
+        side = torch.cuda.Stream()
+        big_src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        big_dst = torch.empty_like(big_src)
+        g16 = lambda i: mxq.mxq_group_scale_fp8(sets[i % len(sets)].x2, offs16, ROW, sets[0].q2, sets[0].sc2, ws, stream)
+        concurrency = {"what": ("group scaling (16640, 5120), 16 groups, row-major, while 1 GiB device copies run "
+                                "on a second stream; per-launch events on the call's stream")}
+        for method in ("hold", "split", "twopass"):
+            with mxq.group_scale_knobs(method=method):
+                for i in range(2):
+                    g16(i)
+                alone = launch_stats(torch, stream, g16, 10)
+                torch.cuda.synchronize()
+                with torch.cuda.stream(side):
+                    for _ in range(8):
+                        big_dst.copy_(big_src)                # about 8 x 0.4 ms of copying queued on the side stream
+                beside = launch_stats(torch, stream, g16, 10)     # issued at once, overlapping the copies
+                entry = {"alone": alone, "beside_streaming_copy": beside}
+                if method == "hold":
+                    t_out, reread = mxq.mxq_group_scale_route_counters(ws, M2, K2, len(ends16), ROW, stream)
+                    entry["last_call_route_counters"] = {"timed_out_tiles": t_out, "tiles_reread_from_x": reread}
+                torch.cuda.synchronize()
+            concurrency[method] = entry
+        del big_src, big_dst, side
     for i in range(2):
         step(i)
     torch.cuda.synchronize()
@@ -754,7 +775,7 @@ def main():
                 "avg_launch_us": round(dom_us, 2)}
 
     # ------------------------------------------------------ grouped GEMM --
-    grouped_mm = None if args.no_gemm else bench_grouped_mm(args, dev, stream, x2_host, ends16, W, mxq, np, torch)
+    grouped_mm = None if "gemm" not in legs else bench_grouped_mm(args, dev, stream, x2_host, ends16, W, mxq, np, torch)
 
     # --------------------------------------------------------- CPU baseline --
     cpu_baseline = None
@@ -839,6 +860,7 @@ def main():
             "groups_row": G_ROW, "groups_col": G_COL, "rotated_buffer_sets": len(sets),
             "step_algorithmic_bytes": step_bytes,
             "transform_overhead_bytes": transform_bytes,
+            "seed": args.seed, "legs": sorted(legs),
         },
         "frac_of_peak": round(value / HBM_PEAK_GBPS, 4),
         "roofline": roofline,
