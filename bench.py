@@ -124,16 +124,16 @@ def grid_transpose(R, C):          # 128 x 128-byte tiles, 256 threads
     return _cdiv(R, 128) * _cdiv(C, 128) * 256
 
 
-def grid_hold(M, K, G):            # (128-row chunks + G + 1 slots) x 512-column strips, 512 threads
-    return (_cdiv(M, 128) + G + 1) * _cdiv(K, 512) * 512
+def grid_hold(M, K, G):            # (128-row chunks + G + 1 slots) x 256-column strips, 256 threads
+    return (_cdiv(M, 128) + G + 1) * _cdiv(K, 256) * 256
 
 
 def grid_finalize(K, G):           # (group, 128-column strip), 256 threads
     return G * _cdiv(K, 128) * 256
 
 
-def grid_col_blocks(M, K):         # 128-row blocks x 512-column strips, 512 threads
-    return _cdiv(M, 128) * _cdiv(K, 512) * 512
+def grid_col_blocks(M, K):         # 128-row blocks x 256-column strips, 256 threads
+    return _cdiv(M, 128) * _cdiv(K, 256) * 256
 
 
 def grid_split_amax(M, K):         # 128-row blocks x 256-column tiles, 256 threads
@@ -194,6 +194,8 @@ def ingest_counters(stats_csv, fetch_csv, write_csv, sq_csv=None, commands=""):
     for G in (16, 32, 64, 128):
         known[("mxq::group_hold_kernel<0>", grid_hold(*T, G))] = (f"(16640, 5120) G={G} row", None)
     known[("mxq::group_amax_kernel<1>", grid_hold(*T, 128))] = ("(16640, 5120) G=128 col", None)
+    known[("mxq::group_hold_kernel<1>", grid_hold(*T, 16))] = ("(16640, 5120) G=16 col", None)
+    known[("mxq::group_hold_kernel<1>", grid_hold(T[0], 8192, 16))] = ("(16640, 8192) dY G=16 col", None)
     known[("mxq::group_finalize_kernel", grid_finalize(T[1], 128))] = ("G=128", None)
     known[("mxq::group_quant_col_blocks_kernel", grid_col_blocks(*T))] = ("(16640, 5120) col", None)
     known[("mxq::group_split_amax_kernel<256>", grid_split_amax(*T))] = ("(16640, 5120)", None)
