@@ -211,10 +211,11 @@ size_t mxq_group_scale_workspace_bytes(int64_t M, int64_t K, int32_t G);
  Three methods, picked on the host from the sizes alone, all giving the same
  * bytes (mxq_set_group_scale_knobs can force any of them):
  *   "hold"    X read once, tiles held on chip until their group's scales are
- *             known: row-major output;
+ *             known: row-major output, and column-major output while the
+ *             average group spans at least eight 128-row blocks;
  *   "split"   two streaming launches (column maxima per 128-row block, then
  *             reduce + quantize): column-major output while the average group
- *             spans at least two 128-row blocks (needs G <= 256);
+ *             spans two to eight 128-row blocks (needs G <= 256);
  *   "two-pass" an amax pass, a finalize pass and a quantize pass: column-major
  *             output with more groups.
  */
