@@ -465,27 +465,58 @@ void mm_tile_kernel(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ 
     stage_barrier<0>();
 
     // epilogue: lane holds D[n][m] for m = c32 and n = 8*(e/4) + 4*hk + e%4
+    if constexpr (F32OUT) {
+        // fp32 (256 KB per tile, more than the LDS): 16-byte stores straight from the accumulators
 #pragma unroll
-    for (int tm = 0; tm < 4; ++tm) {
-        const int m = tl.r0 + 128 * wm + 32 * tm + c32;
-        if (m >= tl.r1) continue;
+        for (int tm = 0; tm < 4; ++tm) {
+            const int m = tl.r0 + 128 * wm + 32 * tm + c32;
+            if (m >= tl.r1) continue;
 #pragma unroll
-        for (int tn = 0; tn < 4; ++tn) {
+            for (int tn = 0; tn < 4; ++tn) {
 #pragma unroll
-            for (int qd = 0; qd < 4; ++qd) {
-                const int n = n0 + 128 * wn + 32 * tn + 8 * qd + 4 * hk;
-                if (n >= N) continue;
-                const v16f& v = acc[tn][tm];
-                if constexpr (F32OUT) {
+                for (int qd = 0; qd < 4; ++qd) {
+                    const int n = n0 + 128 * wn + 32 * tn + 8 * qd + 4 * hk;
+                    if (n >= N) continue;
+                    const v16f& v = acc[tn][tm];
                     float4 o = make_float4(v[4 * qd], v[4 * qd + 1], v[4 * qd + 2], v[4 * qd + 3]);
                     *reinterpret_cast<float4*>(static_cast<float*>(y) + (int64_t)m * N + n) = o;
-                } else {
-                    const v2bf16 lo = {(__bf16)v[4 * qd], (__bf16)v[4 * qd + 1]};
-                    const v2bf16 hi = {(__bf16)v[4 * qd + 2], (__bf16)v[4 * qd + 3]};
-                    uint2 o = make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
-                    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + (int64_t)m * N + n) = o;
                 }
             }
+        }
+    } else {
+        // bf16: the 256 x 256 tile (128 KB) goes through the LDS ring, free now,
+        // so that each lane stores 16 contiguous bytes and a wave writes two
+        // whole 512-byte row segments per instruction (straight from the
+        // accumulators, each store instruction touched 32 rows).  A row is 32
+        // 16-byte units, XOR-swizzled by the row so that the 8-byte writes of a
+        // wave's 32 rows spread over the banks.
+        constexpr int kRowBytes = kBN * 2;
+        const auto unit_of = [](int m, int u) { return (u ^ m) & 31; };
+#pragma unroll
+        for (int tm = 0; tm < 4; ++tm) {
+            const int m = 128 * wm + 32 * tm + c32;
+#pragma unroll
+            for (int tn = 0; tn < 4; ++tn) {
+#pragma unroll
+                for (int qd = 0; qd < 4; ++qd) {
+                    const int u = (128 * wn + 32 * tn + 8 * qd) / 8;     // 16-byte unit of the row
+                    const v16f& v = acc[tn][tm];
+                    const v2bf16 lo = {(__bf16)v[4 * qd], (__bf16)v[4 * qd + 1]};
+                    const v2bf16 hi = {(__bf16)v[4 * qd + 2], (__bf16)v[4 * qd + 3]};
+                    *reinterpret_cast<uint2*>(lds + m * kRowBytes + unit_of(m, u) * 16 + 8 * hk) =
+                        make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+                }
+            }
+        }
+        __syncthreads();
+        const int nrows = tl.r1 - tl.r0;
+        const int u = (int)threadIdx.x & 31;
+        const bool col_ok = n0 + 8 * u < N;
+#pragma unroll 4
+        for (int m = (int)threadIdx.x >> 5; m < kBM; m += kThreads / 32) {
+            if (m >= nrows || !col_ok) continue;
+            const uint4 val = *reinterpret_cast<const uint4*>(lds + m * kRowBytes + unit_of(m, u) * 16);
+            *reinterpret_cast<uint4*>(static_cast<uint16_t*>(y) + (int64_t)(tl.r0 + m) * N + n0 + 8 * u) = val;
         }
     }
 }
