@@ -23,18 +23,27 @@
 //   hold   one workgroup per tile (a 128-row chunk of one group x 256 columns).
 //          It loads its tile into registers, reduces the column maxima (packed
 //          16-bit max of |bf16 bits| -- positive bf16 order is integer order and
-//          Inf/NaN sort above every finite value), publishes them as one row of
-//          partial maxima, and counts itself in.  The last tile of a (group,
-//          strip) to arrive reduces the strip's partial rows, divides and writes
-//          the (G, K) scales; the others poll their scales until written
-//          (bounded by a wall-clock limit) and then quantize the tile still in
-//          their registers: 2 bytes read + 1 byte written per element, nothing
-//          else.  (Folding the maxima with atomic max instead was measured
-//          slower: every tile of a strip hits the same addresses.)
+//          Inf/NaN sort above every finite value) and publishes them as one row
+//          of partial maxima.  The group's last chunk, launched after all the
+//          others, reduces the strip's partial rows, divides and writes the
+//          (G, K) scales; the others poll their scales until written (bounded
+//          by a wall-clock limit) and then quantize the tile still in their
+//          registers: 2 bytes read + 1 byte written per element, nothing else.
+//          (Folding the maxima with atomic max instead was measured slower:
+//          every tile of a strip hits the same addresses.)  If a wait runs out
+//          (the device, perhaps shared with other work, did not keep the
+//          group's tiles resident together), the tiles whose wait ran out
+//          compute the missing chunks' maxima from the input between them and
+//          the first of them publishes the scales.
 //   deferred  tiles of groups too large to hold on chip at once (more tiles than
-//          the device can keep resident), and tiles whose wait ran out, are
-//          re-read and quantized here after the hold kernel has finished, so the
-//          result never depends on how many workgroups are resident.
+//          the device can keep resident) are counted in per (group, strip),
+//          reduced by the last arrival, and re-read and quantized here after the
+//          hold kernel has finished (with this pass launched, tiles whose wait
+//          ran out also leave themselves to it), so the result never depends on
+//          how many workgroups are resident.
+//
+// The two-pass method's kernels (amax, finalize, quantize) are here too; the
+// split method is in group_split.hip.
 //
 // Cross-workgroup data (partial maxima, scales, counters) crosses XCDs, whose
 // L2 caches are not coherent with each other.  An agent-scope fence would write
