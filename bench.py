@@ -193,17 +193,15 @@ def ingest_counters(stats_csv, fetch_csv, write_csv, sq_csv=None, commands=""):
     }
     for G in (16, 32, 64, 128):
         known[("mxq::group_hold_kernel<0>", grid_hold(*T, G))] = (f"(16640, 5120) G={G} row", None)
-    known[("mxq::group_amax_kernel<1>", grid_hold(*T, 128))] = ("(16640, 5120) G=128 col", None)
+    for G in (32, 64, 128):
+        known[("mxq::group_amax_kernel<1, true>", grid_hold(*T, G))] = (f"(16640, 5120) G={G} col", None)
+        known[("mxq::group_finalize_kernel", grid_finalize(T[1], G))] = (f"G={G}", None)
     known[("mxq::group_hold_kernel<1>", grid_hold(*T, 16))] = ("(16640, 5120) G=16 col", None)
     known[("mxq::group_hold_kernel<1>", grid_hold(T[0], 8192, 16))] = ("(16640, 8192) dY G=16 col", None)
-    known[("mxq::group_finalize_kernel", grid_finalize(T[1], 128))] = ("G=128", None)
     known[("mxq::group_quant_col_blocks_kernel", grid_col_blocks(*T))] = ("(16640, 5120) col", None)
-    known[("mxq::group_split_amax_kernel<256>", grid_split_amax(*T))] = ("(16640, 5120)", None)
-    known[("mxq::group_split_quant_kernel<1>", grid_split_quant(*T))] = ("(16640, 5120) col", None)
-    known[("mxq::group_split_amax_kernel<256>", grid_split_amax(T[0], 8192))] = ("(16640, 8192) dY", None)
-    known[("mxq::group_split_quant_kernel<1>", grid_split_quant(T[0], 8192))] = ("(16640, 8192) dY col", None)
+    known[("mxq::group_split_amax_kernel<256>", grid_split_amax(*T))] = ("(16640, 5120), forced", None)
     known[("mxq::group_split_quant_kernel<0>", grid_split_quant(*T))] = ("(16640, 5120) row, forced", None)
-    known[("mxq::group_amax_kernel<0>", grid_hold(*T, 16))] = ("(16640, 5120) G=16 row, forced", None)
+    known[("mxq::group_amax_kernel<0, false>", grid_hold(*T, 16))] = ("(16640, 5120) G=16 row, forced", None)
     known[("mxq::group_quant_kernel<0>", grid_hold(*T, 16))] = ("(16640, 5120) G=16 row, forced", None)
     known[("mxq::group_finalize_kernel", grid_finalize(T[1], 16))] = ("G=16, forced", None)
 
@@ -249,14 +247,13 @@ def ingest_counters(stats_csv, fetch_csv, write_csv, sq_csv=None, commands=""):
     calls = [("group scaling G=16 row-major, hold (plan + hold)",
               [("mxq::group_plan_kernel<128>", None), ("mxq::group_hold_kernel<0>", grid_hold(*T, 16))],
               group_bytes(T[0], T[1], 16)),
-             ("group scaling G=128 column-major, two-pass (plan + amax + finalize + quantize)",
-              [("mxq::group_plan_kernel<128>", None), ("mxq::group_amax_kernel<1>", grid_hold(*T, 128)),
+             ("group scaling G=128 column-major, two-pass (amax with the tables + finalize + quantize)",
+              [("mxq::group_amax_kernel<1, true>", grid_hold(*T, 128)),
                ("mxq::group_finalize_kernel", grid_finalize(T[1], 128)),
                ("mxq::group_quant_col_blocks_kernel", grid_col_blocks(*T))], group_bytes(T[0], T[1], 128)),
-             ("group scaling column-major, split (amax + quantize; mean over its calls at 16, 32 and 64 groups)",
+             ("group scaling G=16 row-major, split forced (amax + quantize)",
               [("mxq::group_split_amax_kernel<256>", grid_split_amax(*T)),
-               ("mxq::group_split_quant_kernel<1>", grid_split_quant(*T))],
-              sum(group_bytes(T[0], T[1], g) for g in (16, 32, 64)) // 3),
+               ("mxq::group_split_quant_kernel<0>", grid_split_quant(*T))], group_bytes(T[0], T[1], 16)),
              ("dispatch pack, top-1 over 16 experts (count + place with the scan folded in + pack)",
               [("mxq::dp_count_kernel", None), ("mxq::dp_place_scan_kernel", None),
                ("mxq::mx_dispatch_pack_kernel", D[0] * 256)], mx_bytes(*D) + 8 * D[0])]

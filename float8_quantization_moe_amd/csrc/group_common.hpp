@@ -168,6 +168,38 @@ __device__ __forceinline__ bool block_any(bool p, uint32_t* votes)
     return r != 0u;
 }
 
+// Inclusive running maximum over the lanes of a wave (values >= 0): DPP row
+// shifts within each 16-lane row, then the row broadcasts.
+__device__ __forceinline__ int dpp_scan_max(int v)
+{
+    const auto mx = [](int a, int b) { return a > b ? a : b; };
+    v = mx(v, __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true));    // row_shr:1
+    v = mx(v, __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true));    // row_shr:2
+    v = mx(v, __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true));    // row_shr:4
+    v = mx(v, __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true));    // row_shr:8
+    v = mx(v, __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false));   // row_bcast:15
+    v = mx(v, __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false));   // row_bcast:31
+    return v;
+}
+// The previous lane's value (0 in lane 0).
+__device__ __forceinline__ int dpp_prev_lane(int v)
+{
+    return __builtin_amdgcn_update_dpp(0, v, 0x138, 0xF, 0xF, true);         // wave_shr:1
+}
+
+// Inclusive sum over the lanes of a wave, with the same DPP row shifts and row
+// broadcasts.
+__device__ __forceinline__ int dpp_scan_add(int v)
+{
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);    // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);    // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);    // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);    // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);   // row_bcast:15
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);   // row_bcast:31
+    return v;
+}
+
 // An opaque copy: the compiler cannot relate the result to its input, so
 // offsets derived from it are recomputed where used instead of being kept in
 // registers from an earlier phase.

@@ -421,6 +421,113 @@ void group_plan_kernel(const int32_t* __restrict__ offs, int G, int M, int K, Wo
     }
 }
 
+// The groups' clamped ends and 128-row chunk ranges, computed by one wave from
+// the device offsets, for up to kInlineGroups groups (4 per lane: group
+// 64 w + l in window w of lane l): the same clamping and chunk numbering as the
+// plan kernel's tables, so the two-pass amax kernel can do without that launch
+// and leave the tables for the passes after it.
+constexpr int kInlineGroups = 256;
+// Size of X from which column-major output holds down to four 128-row blocks
+// per group instead of eight (the method choice below).
+constexpr int64_t kLargeX = (int64_t)512 << 20;
+struct InlineGroups {
+    int e[4], st[4], f[4], n[4];   // end row, start row, first chunk id, chunk count
+    int total;                     // chunks of all groups (ids of rows past the last end follow)
+    int last_end;                  // end of the last group
+    __device__ void build(const int32_t* __restrict__ offs, int G, int M)
+    {
+        const int lane = lane_id();
+        const int nw = (G + kWave - 1) / kWave;     // windows in use
+        int carry_e = 0, carry_f = 0;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            e[w] = carry_e;
+            st[w] = carry_e;
+            f[w] = carry_f;
+            n[w] = 0;
+            if (w >= nw) continue;                  // (uniform)
+            const int g = 64 * w + lane;
+            int v = g < G ? offs[g] : 0;
+            v = dpp_scan_max(v > 0 ? v : 0);
+            v = v > carry_e ? v : carry_e;
+            v = v < M ? v : M;                      // min(M, .) commutes with the running maximum
+            int s0 = dpp_prev_lane(v);
+            if (lane == 0) s0 = carry_e;
+            const int c = (g < G && v > s0) ? ((v + 127) >> 7) - (s0 >> 7) : 0;   // 128-row chunks
+            const int incl = dpp_scan_add(c) + carry_f;
+            e[w] = v;
+            st[w] = s0;
+            n[w] = c;
+            f[w] = incl - c;
+            carry_e = readlane(v, kWave - 1);
+            carry_f = readlane(incl, kWave - 1);
+        }
+        total = carry_f;
+        last_end = carry_e;
+    }
+    // The plan kernel's tables the finalize and column-block passes read: group
+    // ends, chunk ranges, and the group holding the first row of each 128-row
+    // block (G past the last end).  One full wave.
+    __device__ void write_tables(int G, int M, const Workspace& ws) const
+    {
+        const int lane = lane_id();
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const int g = 64 * w + lane;
+            if (g < G) {
+                ws.gend[g] = e[w];
+                ws.gchunks[2 * g] = f[w];
+                ws.gchunks[2 * g + 1] = n[w];
+                for (int c = (st[w] + 127) >> 7; (c << 7) < e[w]; ++c) ws.bfirst[c] = g;
+            }
+        }
+        for (int c = ((last_end + 127) >> 7) + lane; (c << 7) < M; c += kWave) ws.bfirst[c] = G;
+    }
+    // (g is wave-uniform)
+    __device__ int pick(const int (&a)[4], int g) const
+    {
+        const int w = g >> 6, l = g & 63;
+        return w == 0 ? readlane(a[0], l) : w == 1 ? readlane(a[1], l) : w == 2 ? readlane(a[2], l) : readlane(a[3], l);
+    }
+    __device__ int end(int g) const { return pick(e, g); }
+    __device__ int start(int g) const { return g == 0 ? 0 : pick(e, g - 1); }
+    __device__ int first(int g) const { return pick(f, g); }
+    __device__ int count(int g) const { return pick(n, g); }
+    // the group whose chunk range holds chunk id j (wave-uniform), G if none
+    __device__ int group_of_chunk(int j, int G) const
+    {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const unsigned long long m = __ballot(j >= f[w] && j < f[w] + n[w]);
+            if (m) return 64 * w + __builtin_ctzll(m);
+        }
+        return G;
+    }
+};
+
+// Tile (chunk j, strip s) of a group-ordered chunk numbering, from InlineGroups
+// (t.g = G for chunk ids past the last group's chunks).
+template <int R>
+__device__ __forceinline__ TileInfo tile_info_inline(const InlineGroups& gr, int G, int j, int s)
+{
+    TileInfo t;
+    t.g = gr.group_of_chunk(j, G);
+    t.j = j;
+    t.s = s;
+    if (t.g == G) {
+        t.r0 = t.r1 = t.a = t.first = t.count = t.gr0 = t.gr1 = 0;
+        return t;
+    }
+    t.gr0 = gr.start(t.g);
+    t.gr1 = gr.end(t.g);
+    t.first = gr.first(t.g);
+    t.count = gr.count(t.g);
+    t.a = (t.gr0 / R + (j - t.first)) * R;
+    t.r0 = t.gr0 > t.a ? t.gr0 : t.a;
+    t.r1 = t.gr1 < t.a + R ? t.gr1 : t.a + R;
+    return t;
+}
+
 // (kPartialUnset has the top bit set, which no |bf16| maximum has.)
 __device__ __forceinline__ bool partial_written(uint4 w)
 {
@@ -795,14 +902,26 @@ void group_hold_kernel(const uint16_t* __restrict__ x, int M, int K, int G, int 
 // the default cache policy: part of X then still sits in the last-level cache
 // when the quantize pass reads it again (measured 52 -> 44 us for that pass at
 // 16640 x 5120, for 2 us more here).
-template <int LAYOUT>
+// INLINE: the tile comes from the offsets (InlineGroups, G <= kInlineGroups)
+// instead of the plan kernel's table, and workgroup 0 writes the tables the
+// finalize and quantize passes read.
+template <int LAYOUT, bool INLINE>
 __global__ __launch_bounds__(TileCfg<LAYOUT>::T)
-void group_amax_kernel(const uint16_t* __restrict__ x, int K, int G, int S, Workspace ws)
+void group_amax_kernel(const uint16_t* __restrict__ x, int M, int K, const int32_t* __restrict__ offs, int G, int S,
+                       Workspace ws)
 {
     using C = TileCfg<LAYOUT>;
     __shared__ uint4 red[C::NS][C::CG];
     const int j = (int)blockIdx.x / S, s = (int)blockIdx.x % S;
-    const TileInfo t = tile_info<C::R>(ws.table, j, s);
+    TileInfo t;
+    if constexpr (INLINE) {
+        InlineGroups gr;
+        gr.build(offs, G, M);
+        if (blockIdx.x == 0 && threadIdx.x < kWave) gr.write_tables(G, M, ws);   // for the next two passes
+        t = tile_info_inline<C::R>(gr, G, j, s);
+    } else {
+        t = tile_info<C::R>(ws.table, j, s);
+    }
     if (t.g < 0 || t.g == G) return;                      // unused chunk id or rows past the last end (uniform)
     const int cg = (int)threadIdx.x % C::CG, rs = (int)threadIdx.x / C::CG;
     const int k = s * C::W + cg * 8;
@@ -1099,35 +1218,56 @@ static hipError_t launch_layout(const void* x, int M, int K, const int32_t* offs
     // how much longer tiles wait for a strip claimed after a time-out (its
     // claimant reads the group's rows of the strip, one workgroup alone)
     const unsigned long long rescue_ticks = ticks_per_ms * 50ull;
-    // The method.  Default, from measurements at 16640 x 5120 (16 to 128 Zipf
-    // groups): row-major output holds (one read of X; 65-73 us against 75-100 us
-    // for the two-read methods).  Column-major output holds while the average
-    // group spans at least eight 128-row blocks (74 against 76 us at 16 groups),
-    // splits into two streaming passes while it spans at least two (78-84 us
-    // against 84-93 us held: the hold kernel's tiles, cut at group boundaries,
-    // split output lines, and the four-launch two-pass method pays two more
-    // kernel boundaries), and takes the four-launch two-pass method with more
-    // groups (88-91 us against 101 us split and 110 us held: the split method's
-    // quantize pass then reduces several groups per block).
+    // The method.  Default, from measurements at 16640 x 5120 (8 to 128 Zipf
+    // groups), 16640 x 8192 (4 to 32) and 65536 x 5120 (8 to 256).  Row-major
+    // output holds (one read of X; 65-73 us against 75-100 us for the two-read
+    // methods at 16640 x 5120).  Column-major output holds while the average
+    // group spans at least eight 128-row blocks, and takes the two-pass method
+    // with more groups (at 16640 x 5120: 73.5 against 73.7 us at 16 groups,
+    // 76.7 against 75.2 at 20, 110 against 81 at 128).  With a larger X the
+    // hold method's one read pays off to fewer blocks per group: at 65536 x
+    // 5120 (671 MB) it wins down to four (257 against 289 us at 64 groups,
+    // 286 against 294 at 128, 335 against 306 at 256), while at 16640 x 8192
+    // (272 MB) the crossover is still between 16 and 32 groups (115 against
+    // 115, 130 against 116); the threshold of 512 MB lies between the two
+    // sizes measured.  The split method (two streaming passes, the
+    // second over 128-row blocks; at most 256 groups) is taken only when
+    // forced: it was never the fastest, within 1 us of the best at 8 and 16
+    // groups at 16640 x 8192 and 2 to 65 us behind at every other point.
     const int64_t nblk = (M + 127) / 128;
-    bool twopass = LAYOUT == 1 && 5 * (int64_t)G >= nblk;
-    bool split = LAYOUT == 1 && 2 * (int64_t)G <= nblk && 8 * (int64_t)G > nblk && group_split_sizes_ok(M, K, G);
+    const bool large_x = (int64_t)M * K * 2 >= kLargeX;
+    const bool few = 8 * (int64_t)G <= nblk || (large_x && 4 * (int64_t)G <= nblk);
+    bool twopass = LAYOUT == 1 && !few;
+    bool split = false;
     if (kn.method == 1) twopass = split = false;
     if (kn.method == 2) twopass = true, split = false;
     if (kn.method == 3) split = group_split_sizes_ok(M, K, G);
     if (split) return launch_group_split(x, M, K, offs, G, LAYOUT, flags, q, out_scales, workspace, stream);
 
-    // the fills are a few MB: give them enough blocks (the scales are polled
-    // only by the hold kernel)
-    const int nPartial16 = twopass ? 0 : (int)(slots * K / 8);   // (every partial row is written before it is read)
-    const int nScale16 = M > 0 && !twopass ? (int)((int64_t)G * K / 4) : 0;
-    int pgrid = (int)(((int64_t)nPartial16 + nScale16) / (kGThreads * 8));
-    pgrid = pgrid < 64 ? 64 : pgrid > 1024 ? 1024 : pgrid;
-    hipLaunchKernelGGL(group_plan_kernel<C::R>, dim3(pgrid), dim3(kGThreads), 0, stream, offs, G, M, K, ws, nGS,
-                       (int)nTiles, (int)slots, scales, nPartial16, nScale16);
+    // Column-major two-pass with at most kInlineGroups groups: the amax pass
+    // takes the group ends and chunk ranges from the offsets itself, and its
+    // first workgroup writes the tables the finalize and quantize passes read,
+    // so the plan launch (a kernel boundary) is not needed (84 -> 80 us per call
+    // at 16640 x 5120 and 128 groups, measured alternately; every kernel
+    // scanning the offsets itself measured 88 us).
+    const bool inline_groups = M > 0 && twopass && LAYOUT == 1 && G <= kInlineGroups;
+    if (!inline_groups) {
+        // the fills are a few MB: give them enough blocks (the scales are polled
+        // only by the hold kernel)
+        const int nPartial16 = twopass ? 0 : (int)(slots * K / 8);   // (every partial row is written before it is read)
+        const int nScale16 = M > 0 && !twopass ? (int)((int64_t)G * K / 4) : 0;
+        int pgrid = (int)(((int64_t)nPartial16 + nScale16) / (kGThreads * 8));
+        pgrid = pgrid < 64 ? 64 : pgrid > 1024 ? 1024 : pgrid;
+        hipLaunchKernelGGL(group_plan_kernel<C::R>, dim3(pgrid), dim3(kGThreads), 0, stream, offs, G, M, K, ws, nGS,
+                           (int)nTiles, (int)slots, scales, nPartial16, nScale16);
+    }
     if (M > 0 && twopass) {
-        hipLaunchKernelGGL(group_amax_kernel<LAYOUT>, dim3((unsigned)nTiles), dim3(C::T), 0, stream,
-                           (const uint16_t*)x, K, G, S, ws);
+        if (inline_groups)
+            hipLaunchKernelGGL((group_amax_kernel<LAYOUT, true>), dim3((unsigned)nTiles), dim3(C::T), 0, stream,
+                               (const uint16_t*)x, M, K, offs, G, S, ws);
+        else
+            hipLaunchKernelGGL((group_amax_kernel<LAYOUT, false>), dim3((unsigned)nTiles), dim3(C::T), 0, stream,
+                               (const uint16_t*)x, M, K, offs, G, S, ws);
         const int SF = (K + kFW - 1) / kFW;
         hipLaunchKernelGGL(group_finalize_kernel, dim3((unsigned)(G * SF)), dim3(kFThreads), 0, stream, K, SF, ws,
                            scales);

@@ -21,10 +21,11 @@
 //             group also stores the group's scales.
 // No workgroup ever waits for another and no table is built in between: each
 // tile clamps the group ends itself with a DPP wave scan over at most 256
-// offsets, loaded ahead of its tile.  On MI355X each kernel boundary costs
-// about 5 us, so the plan and finalize launches of the earlier two-pass method
-// (four launches in all) were an eighth of the call; here there are two.  X is
-// read twice (5 bytes moved per element against the method's 3).
+// offsets, loaded ahead of its tile.  Two launches, against the two-pass
+// method's three (four with its plan launch); X is read twice (5 bytes moved
+// per element against the method's 3).  Only taken when forced: the two-pass
+// method measured faster wherever this one would apply (16 to 128 groups at
+// 16640 x 5120, 4 to 32 at 16640 x 8192, 8 to 256 at 65536 x 5120).
 //
 // The quantizer needs no clamp: with s = 448 / max(amax, 1e-12) every product
 // x * s is at most 448 (1 + 2^-24) after binary32 rounding, which the E4M3
@@ -50,25 +51,6 @@ constexpr int kWaves = kST / 64;
 // at 16 groups and 35.7 / 36.8 / 39.2 us at 128 groups.
 constexpr int kSplitAmaxWidth = 256;
 static_assert(H == 8 && CG == 16, "tile shape");
-
-// Inclusive running maximum over the lanes of a wave (values >= 0): DPP row
-// shifts within each 16-lane row, then the row broadcasts.
-__device__ __forceinline__ int dpp_scan_max(int v)
-{
-    const auto mx = [](int a, int b) { return a > b ? a : b; };
-    v = mx(v, __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true));    // row_shr:1
-    v = mx(v, __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true));    // row_shr:2
-    v = mx(v, __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true));    // row_shr:4
-    v = mx(v, __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true));    // row_shr:8
-    v = mx(v, __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false));   // row_bcast:15
-    v = mx(v, __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false));   // row_bcast:31
-    return v;
-}
-// The previous lane's value (0 in lane 0).
-__device__ __forceinline__ int dpp_prev_lane(int v)
-{
-    return __builtin_amdgcn_update_dpp(0, v, 0x138, 0xF, 0xF, true);         // wave_shr:1
-}
 
 // The clamped group ends, end(g) = min(M, max(0, offs[0..g])), of all G <= 256
 // groups, held 4 per lane (group 64 j + l in e[j] of lane l) and read with

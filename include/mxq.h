@@ -208,16 +208,18 @@ size_t mxq_group_scale_workspace_bytes(int64_t M, int64_t K, int32_t G);
  * the tile count (about (M/128 + G) * K/512) below 2^31 (MXQ_ERR_SHAPE otherwise).
  * K == 0 is a no-op; M == 0 still writes the (G, K) scales.
  *
- Three methods, picked on the host from the sizes alone, all giving the same
- * bytes (mxq_set_group_scale_knobs can force any of them):
+ * Three methods, all giving the same bytes; the first two are picked on the
+ * host from the sizes alone (mxq_set_group_scale_knobs can force any of them):
  *   "hold"    X read once, tiles held on chip until their group's scales are
  *             known: row-major output, and column-major output while the
- *             average group spans at least eight 128-row blocks;
+ *             average group spans at least eight 128-row blocks (four when X
+ *             is 512 MB or more);
+ *   "two-pass" an amax pass, a finalize pass and a quantize pass, X read
+ *             twice: column-major output with more groups (three launches
+ *             for G <= 256, a fourth, a plan launch, beyond);
  *   "split"   two streaming launches (column maxima per 128-row block, then
- *             reduce + quantize): column-major output while the average group
- *             spans two to eight 128-row blocks (needs G <= 256);
- *   "two-pass" an amax pass, a finalize pass and a quantize pass: column-major
- *             output with more groups.
+ *             reduce + quantize; needs G <= 256): only when forced, as it was
+ *             never measured faster than the other two.
  */
 mxq_status mxq_group_scale_fp8(const void* x_bf16, int64_t M, int64_t K,
                                const int32_t* group_end_offs, int32_t G, int out_layout,
