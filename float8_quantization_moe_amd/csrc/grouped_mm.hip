@@ -31,7 +31,8 @@
 //   row so that the operand reads are free of bank conflicts), filled straight
 //   from global memory by buffer-load-to-LDS.  Each stage waits for its own
 //   loads, reads the wave's operands into VGPRs, and issues its 16 MFMAs with
-//   the loads of the stage three ahead slotted between them.  Global loads use
+//   the loads of the stage three ahead slotted between them; the loop body is
+//   eight stages, one period of the scale-chunk loads.  Global loads use
 //   raw buffer resources that end at the tile's last valid row: rows past a
 //   group's end or past N read as zero, with no per-row branch.  MFMA operand
 //   A is W_g (output columns), B is X (token rows), so each lane ends up holding
@@ -41,6 +42,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <type_traits>
 #include <utility>
 
 #include "device_common.hpp"
@@ -225,20 +227,23 @@ __device__ __forceinline__ void dma16(const v4i& srd, uint32_t lds, uint32_t vof
 // 128-bit wave read); without it they take 4x as long.
 __device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 2) & 3); }
 
-// Loads of stage t, per wave: 2 scale-chunk loads, then 8 data loads into
-// ring slot t % 4.  Stage 0 carries chunk 0 and stage 8c + 4 chunk c + 1 (if
-// that chunk starts before the last stage); other stages issue the 2 chunk
-// loads anyway, out of range and into a sink, and every stage up to the last
-// + 3 issues its 8 data loads (past the real K they read zeros into a slot
-// nobody reads).  So every stage is exactly 10 loads and no branch splits the
-// loop body.
+// Loads of stage t, per wave: 8 data loads into ring slot t % 4, preceded by 2
+// scale-chunk loads on the stages that carry a chunk: stage 0 chunk 0, stage
+// 8c + 4 chunk c + 1 (out of range into a sink if that chunk does not exist).
+// Every stage up to the last + 3 issues its data loads (past the real K they
+// read zeros into a slot nobody reads).  So a stage is 8 or 10 loads, and at
+// the top of stage s the loads of stages s+1 and s+2 (16 or more) are the only
+// ones that may still be in flight.  (Issuing the chunk loads on every stage,
+// 7 of 8 into the sink, kept the count constant at the price of a fifth more
+// load instructions and LDS writes.)
 __device__ __forceinline__ int scale_chunk_of(int t, int nk)
 {
     if (t == 0) return 0;
     if ((t & 7) == 4 && t + 4 < nk) return (t + 4) >> 3;
     return -1;
 }
-constexpr int kLoadsPerStage = 10;
+__device__ __forceinline__ bool carries_chunk(int t) { return t == 0 || (t & 7) == 4; }
+constexpr int kMinLoadsPerStage = 8;
 
 // (KB: bytes per row of the weight scales; ldxs: of the token scales.)
 __device__ __forceinline__ void issue_chunk(int t, int nk, const v4i& wsr, const v4i& xsr, uint32_t KB,
@@ -276,7 +281,7 @@ __device__ __forceinline__ void issue_data(const DataLoads& d, int t)
 __device__ __forceinline__ void issue_stage(int t, int nk, const v4i& wsr, const v4i& xsr, uint32_t KB,
                                             uint32_t ldxs, uint8_t* lds, int wave, int lane, const DataLoads& d)
 {
-    issue_chunk(t, nk, wsr, xsr, KB, ldxs, lds, wave, lane);
+    if (carries_chunk(t)) issue_chunk(t, nk, wsr, xsr, KB, ldxs, lds, wave, lane);
     issue_data<0>(d, t); issue_data<1>(d, t); issue_data<2>(d, t); issue_data<3>(d, t);
     issue_data<4>(d, t); issue_data<5>(d, t); issue_data<6>(d, t); issue_data<7>(d, t);
 }
@@ -292,7 +297,7 @@ __device__ __forceinline__ void stage_barrier()
 
 // Top of stage s: its loads (and all older ones) done; stages s+1 and s+2 may
 // still be in flight.
-__device__ __forceinline__ void stage_wait() { stage_barrier<2 * kLoadsPerStage>(); }
+__device__ __forceinline__ void stage_wait() { stage_barrier<2 * kMinLoadsPerStage>(); }
 
 // One lane's MFMA operand: logical 16-byte chunks c0 and c1 of LDS row r.
 __device__ __forceinline__ v8i read_frag(const uint8_t* tile, int r, int c0, int c1)
@@ -451,15 +456,27 @@ void mm_tile_kernel(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ 
     issue_stage(0, nk, wsr, xsr, KB, ldxs, lds, wave, lane, d);
     issue_stage(1, nk, wsr, xsr, KB, ldxs, lds, wave, lane, d);
     issue_stage(2, nk, wsr, xsr, KB, ldxs, lds, wave, lane, d);
-    for (int s = 0; s < nk; s += 2) {
+    // Eight stages per iteration, so that which of them fetches a scale chunk
+    // (the second, for stage s + 4) is known at compile time: a branch inside
+    // the loop body lets the compiler move a stage's MFMAs past the next
+    // stage's barrier.  The stages of the last partial group of eight fetch no
+    // chunk (there is none after theirs).
+    auto pair = [&](int s, auto chunk) {
         stage_wait();
-        issue_chunk(s + 3, nk, wsr, xsr, KB, ldxs, lds, wave, lane);
         load_scales(sa, sb, lds, s, wn, wm, c32, hk);
         mma_stage<0>(acc, lds, s, wn, wm, c32, hk, sa, sb, d, s + 3);
         stage_wait();
-        issue_chunk(s + 4, nk, wsr, xsr, KB, ldxs, lds, wave, lane);
+        if constexpr (decltype(chunk)::value) issue_chunk(s + 4, nk, wsr, xsr, KB, ldxs, lds, wave, lane);
         mma_stage<1>(acc, lds, s + 1, wn, wm, c32, hk, sa, sb, d, s + 4);
+    };
+    int s = 0;
+    for (; s + 8 <= nk; s += 8) {
+        pair(s, std::true_type{});
+        pair(s + 2, std::false_type{});
+        pair(s + 4, std::false_type{});
+        pair(s + 6, std::false_type{});
     }
+    for (; s < nk; s += 2) pair(s, std::false_type{});
     // the last three stages' loads read zeros into unused slots; let them land
     // before the workgroup's LDS goes away
     stage_barrier<0>();
