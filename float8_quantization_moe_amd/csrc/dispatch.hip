@@ -11,7 +11,9 @@
 //          (column prefix sums over blocks, then the experts' starts) and
 //          writes the cumulative end offsets group_end[e];
 //   place  each pair's rank among the earlier pairs of its block with the same
-//          expert (an LDS scan of the block's 256 ids) gives its row.
+//          expert gives its row: inside a wave, the lanes holding the same id
+//          (one ballot per id bit) below the lane; across waves, per-wave
+//          counts in LDS.
 // For small count tables the scan is folded into the place pass (every place
 // workgroup derives its block's first rows from the whole table), which saves
 // the one-workgroup launch.
@@ -25,6 +27,40 @@ namespace mxq {
 constexpr int kDpThreads = 256;          // pairs per block
 constexpr int kDpScanThreads = 1024;
 constexpr int kDpMaxExperts = 1024;
+constexpr int kDpWaves = kDpThreads / 64;
+
+// Rank of this lane's pair among the earlier pairs of its workgroup with the
+// same expert id e (e < 0: none, rank unused).  wcnt is LDS of kDpWaves x E
+// ints; every thread of the workgroup must call this (it has barriers).
+// Inside a wave the lanes with the same id are found with one ballot per bit
+// of the id (ids are below 2^nbits) and counted below the lane with mbcnt; the
+// lowest lane of each id publishes the wave's count of that id, and the ranks
+// add the counts of the earlier waves.
+__device__ __forceinline__ int rank_in_block(int e, int E, int nbits, int* wcnt)
+{
+    const int tid = (int)threadIdx.x, wave = tid >> 6;
+    for (int i = tid; i < kDpWaves * E; i += kDpThreads) wcnt[i] = 0;
+    unsigned long long m = __ballot(e >= 0);
+    for (int b = 0; b < nbits; ++b) {
+        const bool bit = ((e >> b) & 1) != 0;
+        const unsigned long long bb = __ballot(bit);
+        m &= bit ? bb : ~bb;
+    }
+    const int below = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+    __syncthreads();
+    if (e >= 0 && below == 0) wcnt[wave * E + e] = __builtin_popcountll(m);
+    __syncthreads();
+    int rank = below;
+    for (int w = 0; w < wave; ++w) rank += e >= 0 ? wcnt[w * E + e] : 0;
+    return rank;
+}
+
+__host__ __device__ inline int id_bits(int E)
+{
+    int n = 0;
+    while ((1 << n) < E) ++n;          // ids 0 .. E-1 fit in n bits
+    return n;
+}
 
 __global__ __launch_bounds__(kDpThreads)
 void dp_count_kernel(const int32_t* __restrict__ ids, int64_t P, int E, int32_t* __restrict__ bcount)
@@ -56,6 +92,7 @@ void dp_scan_kernel(int32_t* __restrict__ bcount, int nblk, int E, int32_t* __re
     const int b0 = seg * len, b1 = b0 + len < nblk ? b0 + len : nblk;
     int sum = 0;
     if (mine)
+#pragma unroll 8
         for (int b = b0; b < b1; ++b) sum += bcount[(int64_t)b * E + e];
     if (mine) segsum[seg * E + e] = sum;
     __syncthreads();
@@ -93,17 +130,12 @@ __global__ __launch_bounds__(kDpThreads)
 void dp_place_kernel(const int32_t* __restrict__ ids, int64_t P, int E, const int32_t* __restrict__ bbase,
                      int32_t* __restrict__ src_pair)
 {
-    __shared__ int eid[kDpThreads];
+    __shared__ int wcnt[kDpWaves * kDpMaxExperts];
     const int64_t p = (int64_t)blockIdx.x * kDpThreads + threadIdx.x;
     int e = p < P ? ids[p] : -1;
     e = (e >= 0 && e < E) ? e : -1;
-    eid[threadIdx.x] = e;
-    __syncthreads();
-    if (e >= 0) {
-        int rank = 0;
-        for (int i = 0; i < (int)threadIdx.x; ++i) rank += eid[i] == e ? 1 : 0;
-        src_pair[bbase[(int64_t)blockIdx.x * E + e] + rank] = (int32_t)p;
-    }
+    const int rank = rank_in_block(e, E, id_bits(E), wcnt);
+    if (e >= 0) src_pair[bbase[(int64_t)blockIdx.x * E + e] + rank] = (int32_t)p;
 }
 
 // Scan folded into the place pass, for small tables (nblk * E <= kDpFoldMax,
@@ -120,7 +152,7 @@ void dp_place_scan_kernel(const int32_t* __restrict__ ids, int64_t P, int E, int
                           int32_t* __restrict__ group_end)
 {
     __shared__ int tot[kDpThreads], pre[kDpThreads], start[kDpThreads];
-    __shared__ int eid[kDpThreads];
+    __shared__ int wcnt[kDpWaves * kDpThreads];
     const int tid = (int)threadIdx.x;
     const int b = (int)blockIdx.x;
     const int S = kDpThreads / E;                        // segments per expert (>= 1)
@@ -134,7 +166,8 @@ void dp_place_scan_kernel(const int32_t* __restrict__ ids, int64_t P, int E, int
         const int len = (nblk + S - 1) / S;
         const int b0 = seg * len, b1 = b0 + len < nblk ? b0 + len : nblk;
         int t_sum = 0, p_sum = 0;
-        for (int bb = b0; bb < b1; ++bb) {
+#pragma unroll 8
+        for (int bb = b0; bb < b1; ++bb) {              // (unrolled: the L2 loads go out together)
             const int c = bcount[(int64_t)bb * E + e0];
             t_sum += c;
             p_sum += bb < b ? c : 0;
@@ -158,13 +191,8 @@ void dp_place_scan_kernel(const int32_t* __restrict__ ids, int64_t P, int E, int
     const int64_t p = (int64_t)b * kDpThreads + tid;
     int e = p < P ? ids[p] : -1;
     e = (e >= 0 && e < E) ? e : -1;
-    eid[tid] = e;
-    __syncthreads();
-    if (e >= 0) {
-        int rank = 0;
-        for (int i = 0; i < tid; ++i) rank += eid[i] == e ? 1 : 0;
-        src_pair[start[e] - tot[e] + pre[e] + rank] = (int32_t)p;
-    }
+    const int rank = rank_in_block(e, E, id_bits(E), wcnt);
+    if (e >= 0) src_pair[start[e] - tot[e] + pre[e] + rank] = (int32_t)p;
 }
 
 int dispatch_max_experts() { return kDpMaxExperts; }

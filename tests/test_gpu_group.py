@@ -336,3 +336,39 @@ def test_concurrent_calls_on_separate_streams():
     wq, ws = U.oracle_mx_quantize(xm_bits)
     assert np.array_equal(U.host_u8(qm), wq) and np.array_equal(U.host_u8(sm), ws)
     assert np.array_equal(U.host_u16(ym), U.oracle_mx_dequantize(wq, ws))
+
+
+@pytest.mark.parametrize("G", [32, 128, 256, 300])
+def test_automatic_method_around_the_large_input_rule(G):
+    """(65536, 5120) bf16 tokens, 671 MB, with the automatic method choice: 32
+    groups hold (at least eight 128-row blocks per group), 128 groups hold under
+    the rule for inputs of 512 MB or more (four blocks per group), 256 groups take
+    the two-pass method with its tables built in the amax pass, and 300 groups the
+    two-pass method with its plan launch.  Whole sampled columns, both layouts,
+    against the oracle (columns are independent)."""
+    M, K = 65536, 5120
+    print(f"group scaling M={M} K={K} G={G} automatic", flush=True)
+    x = W.device_tokens(M, K, seed=31)
+    ends = W.zipf_group_ends(M, G, seed=3)
+    offs = torch.from_numpy(ends).cuda()
+    ws = torch.empty(mxq.mxq_group_scale_workspace_bytes(M, K, G), dtype=torch.uint8, device="cuda")
+    ws.fill_(0xAB)
+    out = {}
+    for layout in (ROW, COL):
+        qg = U.Guarded(M * K, torch.uint8, (M, K) if layout == ROW else (K, M))
+        sg = U.Guarded(G * K, torch.float32, (G, K))
+        mxq.mxq_group_scale_fp8(x, offs, layout, qg.t, sg.t, ws)
+        torch.cuda.synchronize()
+        assert qg.guard_intact() and sg.guard_intact(), "wrote past the end"
+        out[layout] = (qg, sg)
+    rng = np.random.default_rng(G)
+    cols_np = np.array(sorted(set([0, 1, 7, 8, K - 8, K - 1] + rng.integers(0, K, 10).tolist())), np.int64)
+    cols = torch.from_numpy(cols_np).cuda()
+    xb = np.ascontiguousarray(U.host_u16(x.index_select(1, cols)))
+    want_q, want_s = oracle.group_scale(xb, ends, oracle.LAYOUT_ROW)
+    want_s = want_s.view(np.uint32)
+    for layout, (qg, sg) in out.items():
+        got_s = U.host_f32_bits(sg.t.index_select(1, cols))
+        assert np.array_equal(got_s, want_s), f"layout {layout} scales: {U.first_mismatch(got_s, want_s)}"
+        got_q = U.host_u8(qg.t.index_select(1, cols)) if layout == ROW else U.host_u8(qg.t.index_select(0, cols)).T
+        assert np.array_equal(got_q, want_q), f"layout {layout} codes: {U.first_mismatch(got_q, want_q)}"
