@@ -13,9 +13,10 @@
 // parallel", Summary (the MXFP8 buffers of the token exchange).
 //
 // Work decomposition
-//   Output tiles are 256 token rows x 256 columns.  Row tiles never straddle a
-//   group: group g's rows [start, end) are cut into ceil(len/256) tiles from
-//   its start, so a tile reads one W_g.  Rows past the last end form one more
+//   Output tiles are up to 256 token rows x 256 columns.  Row tiles never
+//   straddle a group: group g's rows [start, end) are cut into ceil(len/256)
+//   tiles from its start, so a tile reads one W_g; the last one runs at the
+//   smallest height of 64, 128, 192 or 256 rows that holds its rows.  Rows past the last end form one more
 //   pseudo-group whose tiles are written with zeros.  A one-workgroup plan
 //   kernel turns the device-resident end offsets into this tile list (no host
 //   copy), ordered group by group, and inside a group in blocks of kCB column
@@ -25,12 +26,13 @@
 //   workgroups to the 8 XCDs round-robin, so each XCD walks one contiguous
 //   stretch of the list and its L2 sees the reuse.
 //
-// Tile kernel (256 threads = 4 waves in 2 x 2, each wave 128 x 128)
+// Tile kernel (256 threads = 4 waves; for 256-row tiles in 2 x 2, each wave
+// 128 x 128)
 //   K advances 64 bytes (one MFMA k-step) per stage through a 4-slot LDS ring
-//   of W_g and X tiles (256 rows x 64 B each; 16-byte chunks XOR-swizzled by
+//   of W_g and X tiles (up to 256 rows x 64 B each; 16-byte chunks XOR-swizzled by
 //   row so that the operand reads are free of bank conflicts), filled straight
 //   from global memory by buffer-load-to-LDS.  Each stage waits for its own
-//   loads, reads the wave's operands into VGPRs, and issues its 16 MFMAs with
+//   loads, reads the wave's operands into VGPRs, and issues its MFMAs with
 //   the loads of the stage three ahead slotted between them; the loop body is
 //   eight stages, one period of the scale-chunk loads.  Global loads use
 //   raw buffer resources that end at the tile's last valid row: rows past a
@@ -227,13 +229,14 @@ __device__ __forceinline__ void dma16(const v4i& srd, uint32_t lds, uint32_t vof
 // 128-bit wave read); without it they take 4x as long.
 __device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 2) & 3); }
 
-// Loads of stage t, per wave: 8 data loads into ring slot t % 4, preceded by 2
-// scale-chunk loads on the stages that carry a chunk: stage 0 chunk 0, stage
-// 8c + 4 chunk c + 1 (out of range into a sink if that chunk does not exist).
-// Every stage up to the last + 3 issues its data loads (past the real K they
-// read zeros into a slot nobody reads).  So a stage is 8 or 10 loads, and at
-// the top of stage s the loads of stages s+1 and s+2 (16 or more) are the only
-// ones that may still be in flight.  (Issuing the chunk loads on every stage,
+// Loads of stage t, per wave: its data loads (NL of them: 8 for 256-row tiles,
+// 6 for 128-row tiles) into ring slot t % 4, preceded by 2 scale-chunk loads on
+// the stages that carry a chunk: stage 0 chunk 0, stage 8c + 4 chunk c + 1 (out
+// of range into a sink if that chunk does not exist).  Every stage up to the
+// last + 3 issues its data loads (past the real K they read zeros into a slot
+// nobody reads).  So a stage is NL or NL + 2 loads, and at the top of stage s
+// the loads of stages s+1 and s+2 (2 NL or more) are the only ones that may
+// still be in flight.  (Issuing the chunk loads on every stage,
 // 7 of 8 into the sink, kept the count constant at the price of a fifth more
 // load instructions and LDS writes.)
 __device__ __forceinline__ int scale_chunk_of(int t, int nk)
@@ -243,7 +246,6 @@ __device__ __forceinline__ int scale_chunk_of(int t, int nk)
     return -1;
 }
 __device__ __forceinline__ bool carries_chunk(int t) { return t == 0 || (t & 7) == 4; }
-constexpr int kMinLoadsPerStage = 8;
 
 // (KB: bytes per row of the weight scales; ldxs: of the token scales.)
 __device__ __forceinline__ void issue_chunk(int t, int nk, const v4i& wsr, const v4i& xsr, uint32_t KB,
@@ -257,33 +259,63 @@ __device__ __forceinline__ void issue_chunk(int t, int nk, const v4i& wsr, const
     dma16(xsr, c >= 0 ? real + kChunkBytes : sink, c >= 0 ? row * ldxs + (uint32_t)c * 16u : kOOB);
 }
 
+// The wave layout of a tile of BM token rows x 256 output columns.  A group's
+// rows are cut into 256-row tiles from its start, and its last tile takes the
+// smallest height of 64, 128, 192 and 256 that holds its rows, so that a short
+// tile does less MFMA work and fewer loads instead of padding to 256 rows with
+// zeros.  256 and 192 rows: 4 waves in 2 x 2, each 128 W rows x 128 (96)
+// token rows, 4 x 4 (4 x 3) MFMA tiles.  128 and 64 rows: 4 waves side by side
+// over the columns, each 64 W rows x 128 (64) token rows, 2 x 4 (2 x 2).
+template <int BM>
+struct MmShape {
+    static_assert(BM == 256 || BM == 192 || BM == 128 || BM == 64, "64- to 256-row tiles");
+    static constexpr bool kSquare = BM >= 192;         // 2 x 2 waves (else 4 x 1)
+    static constexpr int TN = kSquare ? 4 : 2;         // 32-row W tiles per wave
+    static constexpr int TM = kSquare ? BM / 64 : BM / 32;   // 32-row token tiles per wave
+    static constexpr int XL = BM / 64;                 // token-row data loads per wave and stage
+    static constexpr int NL = 4 + XL;                  // data loads per wave and stage (W: 4)
+    static constexpr int NM = TN * TM;                 // MFMAs per wave and stage
+    __device__ static int wn(int wave) { return kSquare ? wave >> 1 : wave; }
+    __device__ static int wm(int wave) { return kSquare ? wave & 1 : 0; }
+};
+
 // Per-wave state of the data loads: the lane's offset of load i (rows
-// 64*wave + 16*i .. +15, its swizzled 16-byte chunk) and the LDS address of
-// the wave's first row in slot 0.
+// 64*wave + 16*i .. +15 of W, (BM/4)*wave + 16*i .. of X, its swizzled 16-byte
+// chunk) and the LDS addresses of the wave's first W and X rows in slot 0.
 struct DataLoads {
     v4i wr, xr;
     uint32_t off[4];          // weight rows (stride K)
     uint32_t offx[4];         // token rows (stride ldx)
-    uint32_t lds0;
+    uint32_t ldsw, ldsx;
     int nk;
 };
 
-// Data load k (0..7) of stage t: rows of load k/2 of A (k even) or B.
-template <int KL>
+// Data load KL of stage t: W and X loads alternate while both last (W0 X0 W1
+// X1 ...), then the remaining W loads.
+template <int XL, int KL>
 __device__ __forceinline__ void issue_data(const DataLoads& d, int t)
 {
-    constexpr int i = KL >> 1, op = KL & 1;
-    const uint32_t dst = d.lds0 + (uint32_t)(t & (kRing - 1)) * 2 * kTileBytes + op * kTileBytes + 16 * i * kBK;
+    constexpr bool pair = KL < 2 * XL;
+    constexpr int op = pair ? (KL & 1) : 0;
+    constexpr int i = pair ? (KL >> 1) : KL - XL;
+    const uint32_t dst = (op == 0 ? d.ldsw : d.ldsx) + (uint32_t)(t & (kRing - 1)) * 2 * kTileBytes + 16 * i * kBK;
     const uint32_t off = t < d.nk ? (op == 0 ? d.off[i] : d.offx[i]) + (uint32_t)t * kBK : kOOB;
     dma16(op == 0 ? d.wr : d.xr, dst, off);
 }
 
+template <int XL, int... KL>
+__device__ __forceinline__ void issue_data_all(const DataLoads& d, int t, std::integer_sequence<int, KL...>)
+{
+    (issue_data<XL, KL>(d, t), ...);
+}
+
+template <int BM>
 __device__ __forceinline__ void issue_stage(int t, int nk, const v4i& wsr, const v4i& xsr, uint32_t KB,
                                             uint32_t ldxs, uint8_t* lds, int wave, int lane, const DataLoads& d)
 {
+    using S = MmShape<BM>;
     if (carries_chunk(t)) issue_chunk(t, nk, wsr, xsr, KB, ldxs, lds, wave, lane);
-    issue_data<0>(d, t); issue_data<1>(d, t); issue_data<2>(d, t); issue_data<3>(d, t);
-    issue_data<4>(d, t); issue_data<5>(d, t); issue_data<6>(d, t); issue_data<7>(d, t);
+    issue_data_all<S::XL>(d, t, std::make_integer_sequence<int, S::NL>{});
 }
 
 // Wait until at most N of this wave's buffer loads are outstanding and its LDS
@@ -295,9 +327,10 @@ __device__ __forceinline__ void stage_barrier()
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-// Top of stage s: its loads (and all older ones) done; stages s+1 and s+2 may
-// still be in flight.
-__device__ __forceinline__ void stage_wait() { stage_barrier<2 * kMinLoadsPerStage>(); }
+// Top of stage s: its loads (and all older ones) done; stages s+1 and s+2 (at
+// least 2 NL loads) may still be in flight.
+template <int BM>
+__device__ __forceinline__ void stage_wait() { stage_barrier<2 * MmShape<BM>::NL>(); }
 
 // One lane's MFMA operand: logical 16-byte chunks c0 and c1 of LDS row r.
 __device__ __forceinline__ v8i read_frag(const uint8_t* tile, int r, int c0, int c1)
@@ -308,74 +341,85 @@ __device__ __forceinline__ v8i read_frag(const uint8_t* tile, int r, int c0, int
     return v;
 }
 
-// acc[tn][tm] += A-tile tn x B-tile tm for all 16 pairs.  Operands are E4M3
-// (format code 0 for both); op_sel OPS picks the byte of sa[tn] / sb[tm] that
-// holds the E8M0 scale of the lane's row and k-block.
-template <int TN, int TM, int OPS>
-__device__ __forceinline__ void mma_tiles(v16f (&acc)[4][4], const v8i (&a)[4], const v8i (&b)[4], const int (&sa)[4],
-                                          const int (&sb)[4])
+// MFMA I of the wave's TN x TM tiles of stage s = 2p + Q, then the data loads
+// of stage t that fall after it.  Lane (c32, hk) holds, of the 64 k of the
+// stage, the bytes k = 16*hk .. +15 and 32 + 16*hk .. +15 (chunks hk and
+// 2 + hk) of its row, and its scale byte covers the 32-k block hk: block
+// 4p + 2Q + hk of the row, which is byte 2Q of the pair's scale word shifted
+// right by 8*hk.  Load j goes after MFMA (2j + 1) NM / (2 NL) (rounded down):
+// with 16 MFMAs and 8 loads, one after every other MFMA (measured 2 % faster
+// than one after each of the first 8, and than all 8 before the MFMAs).
+template <int BM, int J>
+__device__ __forceinline__ constexpr int load_slot()
 {
-    acc[TN][TM] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[TN], b[TM], acc[TN][TM], 0, 0, OPS, sa[TN], OPS,
-                                                                  sb[TM]);
-    if constexpr (TM + 1 < 4) mma_tiles<TN, TM + 1, OPS>(acc, a, b, sa, sb);
-    else if constexpr (TN + 1 < 4) mma_tiles<TN + 1, 0, OPS>(acc, a, b, sa, sb);
+    return (2 * J + 1) * MmShape<BM>::NM / (2 * MmShape<BM>::NL);
 }
 
-// Stage s = 2p + Q.  Lane (c32, hk) holds, of the 64 k of the stage, the bytes
-// k = 16*hk .. +15 and 32 + 16*hk .. +15 (chunks hk and 2 + hk) of its row, and
-// its scale byte covers the 32-k block hk: block 4p + 2Q + hk of the row, which
-// is byte 2Q of the pair's scale word shifted right by 8*hk.
-// MFMA I of the wave's 4 x 4 tiles, then (odd I) data load I/2 of stage t.
-template <int Q, int I>
-__device__ __forceinline__ void mma_step(v16f (&acc)[4][4], const v8i (&a)[4], const v8i (&b)[4], const int (&sa)[4],
-                                         const int (&sb)[4], const DataLoads& d, int t)
+template <int BM, int I, int J>
+__device__ __forceinline__ void loads_after(const DataLoads& d, int t)
 {
-    constexpr int tn = I >> 2, tm = I & 3;
+    if constexpr (J < MmShape<BM>::NL) {
+        if constexpr (load_slot<BM, J>() == I) issue_data<MmShape<BM>::XL, J>(d, t);
+        loads_after<BM, I, J + 1>(d, t);
+    }
+}
+
+template <int BM, int Q, int I>
+__device__ __forceinline__ void mma_step(v16f (&acc)[MmShape<BM>::TN][MmShape<BM>::TM],
+                                         const v8i (&a)[MmShape<BM>::TN], const v8i (&b)[MmShape<BM>::TM],
+                                         const int (&sa)[MmShape<BM>::TN], const int (&sb)[MmShape<BM>::TM],
+                                         const DataLoads& d, int t)
+{
+    constexpr int tn = I / MmShape<BM>::TM, tm = I % MmShape<BM>::TM;
     acc[tn][tm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[tn], b[tm], acc[tn][tm], 0, 0, 2 * Q, sa[tn],
                                                                   2 * Q, sb[tm]);
-    if constexpr (I % 2 == 1) issue_data<I / 2>(d, t);
+    loads_after<BM, I, 0>(d, t);
     __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int Q, int... Is>
-__device__ __forceinline__ void mma_steps(v16f (&acc)[4][4], const v8i (&a)[4], const v8i (&b)[4], const int (&sa)[4],
-                                          const int (&sb)[4], const DataLoads& d, int t, std::integer_sequence<int, Is...>)
+template <int BM, int Q, int... Is>
+__device__ __forceinline__ void mma_steps(v16f (&acc)[MmShape<BM>::TN][MmShape<BM>::TM],
+                                          const v8i (&a)[MmShape<BM>::TN], const v8i (&b)[MmShape<BM>::TM],
+                                          const int (&sa)[MmShape<BM>::TN], const int (&sb)[MmShape<BM>::TM],
+                                          const DataLoads& d, int t, std::integer_sequence<int, Is...>)
 {
-    (mma_step<Q, Is>(acc, a, b, sa, sb, d, t), ...);
+    (mma_step<BM, Q, Is>(acc, a, b, sa, sb, d, t), ...);
 }
 
-// Stage s = 2p + Q: read its operands from LDS, then issue its 16 MFMAs with
-// the 8 data loads of stage t = s + 3 slotted one after every other MFMA (the
-// loads' issue stalls then overlap the matrix core; measured 2 % faster than
-// one after each of the first 8, and than all 8 before the MFMAs).
-template <int Q>
-__device__ __forceinline__ void mma_stage(v16f (&acc)[4][4], const uint8_t* lds, int s, int wn, int wm, int c32,
-                                          int hk, const int (&sa)[4], const int (&sb)[4], const DataLoads& d, int t)
+// Stage s = 2p + Q: read its operands from LDS (the wave's W rows from wrow,
+// its token rows from xrow), then issue its MFMAs with the data loads of stage
+// t = s + 3 slotted between them.
+template <int BM, int Q>
+__device__ __forceinline__ void mma_stage(v16f (&acc)[MmShape<BM>::TN][MmShape<BM>::TM], const uint8_t* lds, int s,
+                                          int wrow, int xrow, int c32, int hk, const int (&sa)[MmShape<BM>::TN],
+                                          const int (&sb)[MmShape<BM>::TM], const DataLoads& d, int t)
 {
+    using S = MmShape<BM>;
     const uint8_t* A = lds + (s & (kRing - 1)) * 2 * kTileBytes;
     const uint8_t* B = A + kTileBytes;
-    v8i a[4], b[4];
+    v8i a[S::TN], b[S::TM];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = read_frag(A, 128 * wn + 32 * i + c32, hk, 2 + hk);
+    for (int i = 0; i < S::TN; ++i) a[i] = read_frag(A, wrow + 32 * i + c32, hk, 2 + hk);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) b[i] = read_frag(B, 128 * wm + 32 * i + c32, hk, 2 + hk);
+    for (int i = 0; i < S::TM; ++i) b[i] = read_frag(B, xrow + 32 * i + c32, hk, 2 + hk);
     __builtin_amdgcn_sched_barrier(0);
-    mma_steps<Q>(acc, a, b, sa, sb, d, t, std::make_integer_sequence<int, 16>{});
+    mma_steps<BM, Q>(acc, a, b, sa, sb, d, t, std::make_integer_sequence<int, S::NM>{});
 }
 
-// Scale words of the pair of stage s (s even) for the lane's four A and B
+// Scale words of the pair of stage s (s even) for the lane's W and token
 // tiles: word (s % 8) / 2 of each row's 16-byte chunk, shifted so that byte 2Q
 // is the lane's k-block.
-__device__ __forceinline__ void load_scales(int (&sa)[4], int (&sb)[4], const uint8_t* lds, int s, int wn, int wm,
-                                            int c32, int hk)
+template <int BM>
+__device__ __forceinline__ void load_scales(int (&sa)[MmShape<BM>::TN], int (&sb)[MmShape<BM>::TM], const uint8_t* lds,
+                                            int s, int wrow, int xrow, int c32, int hk)
 {
     const uint8_t* sl = lds + kDataBytes + ((s >> 3) & 1) * 2 * kChunkBytes + ((s & 7) >> 1) * 4;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        sa[i] = (int)(*reinterpret_cast<const uint32_t*>(sl + (128 * wn + 32 * i + c32) * 16) >> (8 * hk));
-        sb[i] = (int)(*reinterpret_cast<const uint32_t*>(sl + kChunkBytes + (128 * wm + 32 * i + c32) * 16) >>
-                      (8 * hk));
-    }
+    for (int i = 0; i < MmShape<BM>::TN; ++i)
+        sa[i] = (int)(*reinterpret_cast<const uint32_t*>(sl + (wrow + 32 * i + c32) * 16) >> (8 * hk));
+#pragma unroll
+    for (int i = 0; i < MmShape<BM>::TM; ++i)
+        sb[i] = (int)(*reinterpret_cast<const uint32_t*>(sl + kChunkBytes + (xrow + 32 * i + c32) * 16) >> (8 * hk));
 }
 
 __device__ __forceinline__ void zero_tile(void* y, int N, int r0, int r1, int n0, bool f32)
@@ -389,6 +433,132 @@ __device__ __forceinline__ void zero_tile(void* y, int N, int r0, int r1, int n0
         const int u = i % per_row;
         uint8_t* p = static_cast<uint8_t*>(y) + ((int64_t)r * N + n0) * esz + u * 16;
         *reinterpret_cast<uint4*>(p) = make_uint4(0, 0, 0, 0);
+    }
+}
+
+// The K loop and the epilogue of one tile of BM token rows (rows [r0, r1) of
+// group g's operand, at most BM of them) x 256 columns from n0.
+template <int BM, bool F32OUT>
+__device__ __forceinline__ void tile_product(uint8_t* lds, const v4i& wr, const v4i& xr, const v4i& wsr, const v4i& xsr,
+                                             uint32_t uK, uint32_t ldx, uint32_t KB, uint32_t ldxs, int N, int K,
+                                             int r0, int r1, int n0, void* __restrict__ y)
+{
+    using S = MmShape<BM>;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int wrow = 32 * S::TN * S::wn(wave);   // the wave's first W row (output column) of the tile
+    const int xrow = 32 * S::TM * S::wm(wave);   // its first token row
+    const int c32 = lane & 31;
+    const int hk = lane >> 5;
+
+    v16f acc[S::TN][S::TM];
+#pragma unroll
+    for (int i = 0; i < S::TN; ++i)
+#pragma unroll
+        for (int j = 0; j < S::TM; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+    // Pipeline: stages 0..2 in flight before the loop; the top of stage s
+    // waits for stage s (loads complete in issue order, and the scale chunk of
+    // s was issued with an earlier stage) and frees slot s-1 for stage s+3.
+    const int nk = K / kBK;                      // even, >= 2
+    DataLoads d;
+    d.wr = wr;
+    d.xr = xr;
+    d.nk = nk;
+    d.ldsw = lds_addr(lds + 64 * wave * kBK);
+    d.ldsx = lds_addr(lds + kTileBytes + (BM / 4) * wave * kBK);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = 64 * wave + 16 * i + (lane >> 2);
+        d.off[i] = (uint32_t)row * uK + ((uint32_t)swz(row, lane & 3) << 4);
+        const int rowx = (BM / 4) * wave + 16 * i + (lane >> 2);
+        d.offx[i] = (uint32_t)rowx * ldx + ((uint32_t)swz(rowx, lane & 3) << 4);
+    }
+    int sa[S::TN], sb[S::TM];
+    issue_stage<BM>(0, nk, wsr, xsr, KB, ldxs, lds, wave, lane, d);
+    issue_stage<BM>(1, nk, wsr, xsr, KB, ldxs, lds, wave, lane, d);
+    issue_stage<BM>(2, nk, wsr, xsr, KB, ldxs, lds, wave, lane, d);
+    // Eight stages per iteration, so that which of them fetches a scale chunk
+    // (the second, for stage s + 4) is known at compile time: a branch inside
+    // the loop body lets the compiler move a stage's MFMAs past the next
+    // stage's barrier.  The stages of the last partial group of eight fetch no
+    // chunk (there is none after theirs).
+    auto pair = [&](int s, auto chunk) {
+        stage_wait<BM>();
+        load_scales<BM>(sa, sb, lds, s, wrow, xrow, c32, hk);
+        mma_stage<BM, 0>(acc, lds, s, wrow, xrow, c32, hk, sa, sb, d, s + 3);
+        stage_wait<BM>();
+        if constexpr (decltype(chunk)::value) issue_chunk(s + 4, nk, wsr, xsr, KB, ldxs, lds, wave, lane);
+        mma_stage<BM, 1>(acc, lds, s + 1, wrow, xrow, c32, hk, sa, sb, d, s + 4);
+    };
+    int s = 0;
+    for (; s + 8 <= nk; s += 8) {
+        pair(s, std::true_type{});
+        pair(s + 2, std::false_type{});
+        pair(s + 4, std::false_type{});
+        pair(s + 6, std::false_type{});
+    }
+    for (; s < nk; s += 2) pair(s, std::false_type{});
+    // the last three stages' loads read zeros into unused slots; let them land
+    // before the workgroup's LDS goes away
+    stage_barrier<0>();
+
+    // epilogue: lane holds D[n][m] for m = c32 and n = 8*(e/4) + 4*hk + e%4
+    if constexpr (F32OUT) {
+        // fp32 (256 KB per 256-row tile, more than the LDS): 16-byte stores straight from the accumulators
+#pragma unroll
+        for (int tm = 0; tm < S::TM; ++tm) {
+            const int m = r0 + xrow + 32 * tm + c32;
+            if (m >= r1) continue;
+#pragma unroll
+            for (int tn = 0; tn < S::TN; ++tn) {
+#pragma unroll
+                for (int qd = 0; qd < 4; ++qd) {
+                    const int n = n0 + wrow + 32 * tn + 8 * qd + 4 * hk;
+                    if (n >= N) continue;
+                    const v16f& v = acc[tn][tm];
+                    float4 o = make_float4(v[4 * qd], v[4 * qd + 1], v[4 * qd + 2], v[4 * qd + 3]);
+                    *reinterpret_cast<float4*>(static_cast<float*>(y) + (int64_t)m * N + n) = o;
+                }
+            }
+        }
+    } else {
+        // bf16: the BM x 256 tile (up to 128 KB) goes through the LDS ring, free
+        // now, so that each lane stores 16 contiguous bytes and a wave writes
+        // two whole 512-byte row segments per instruction (straight from the
+        // accumulators, each store instruction touched 32 rows).  A row is 32
+        // 16-byte units, XOR-swizzled by the row so that the 8-byte writes of a
+        // wave's 32 rows spread over the banks.
+        constexpr int kRowBytes = kBN * 2;
+        const auto unit_of = [](int m, int u) { return (u ^ m) & 31; };
+#pragma unroll
+        for (int tm = 0; tm < S::TM; ++tm) {
+            const int m = xrow + 32 * tm + c32;
+#pragma unroll
+            for (int tn = 0; tn < S::TN; ++tn) {
+#pragma unroll
+                for (int qd = 0; qd < 4; ++qd) {
+                    const int u = (wrow + 32 * tn + 8 * qd) / 8;     // 16-byte unit of the row
+                    const v16f& v = acc[tn][tm];
+                    const v2bf16 lo = {(__bf16)v[4 * qd], (__bf16)v[4 * qd + 1]};
+                    const v2bf16 hi = {(__bf16)v[4 * qd + 2], (__bf16)v[4 * qd + 3]};
+                    *reinterpret_cast<uint2*>(lds + m * kRowBytes + unit_of(m, u) * 16 + 8 * hk) =
+                        make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+                }
+            }
+        }
+        __syncthreads();
+        const int nrows = r1 - r0;
+        const int u = (int)threadIdx.x & 31;
+        const bool col_ok = n0 + 8 * u < N;
+#pragma unroll 4
+        for (int m = (int)threadIdx.x >> 5; m < BM; m += kThreads / 32) {
+            if (m >= nrows || !col_ok) continue;
+            const uint4 val = *reinterpret_cast<const uint4*>(lds + m * kRowBytes + unit_of(m, u) * 16);
+            *reinterpret_cast<uint4*>(static_cast<uint16_t*>(y) + (int64_t)(r0 + m) * N + n0 + 8 * u) = val;
+        }
     }
 }
 
@@ -421,121 +591,15 @@ void mm_tile_kernel(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ 
     const v4i xr = make_srd(xq + (size_t)tl.r0 * ldx, (uint32_t)nrows_x * ldx);
     const v4i wsr = make_srd(wsc + wrow0 * KB, (uint32_t)nrows_w * KB);
     const v4i xsr = make_srd(xs + (size_t)tl.r0 * ldxs, (uint32_t)nrows_x * ldxs);
-
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int wn = wave >> 1;                    // W rows (output columns) 128*wn ..
-    const int wm = wave & 1;                     // X rows (tokens) 128*wm ..
-    const int c32 = lane & 31;
-    const int hk = lane >> 5;
-
-    v16f acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-
-    // Pipeline: stages 0..2 in flight before the loop; the top of stage s
-    // waits for stage s (loads complete in issue order, and the scale chunk of
-    // s was issued with an earlier stage) and frees slot s-1 for stage s+3.
-    const int nk = K / kBK;                      // even, >= 2
-    DataLoads d;
-    d.wr = wr;
-    d.xr = xr;
-    d.nk = nk;
-    d.lds0 = lds_addr(lds + 64 * wave * kBK);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int row = 64 * wave + 16 * i + (lane >> 2);
-        d.off[i] = (uint32_t)row * uK + ((uint32_t)swz(row, lane & 3) << 4);
-        d.offx[i] = (uint32_t)row * ldx + ((uint32_t)swz(row, lane & 3) << 4);
-    }
-    int sa[4], sb[4];
-    issue_stage(0, nk, wsr, xsr, KB, ldxs, lds, wave, lane, d);
-    issue_stage(1, nk, wsr, xsr, KB, ldxs, lds, wave, lane, d);
-    issue_stage(2, nk, wsr, xsr, KB, ldxs, lds, wave, lane, d);
-    // Eight stages per iteration, so that which of them fetches a scale chunk
-    // (the second, for stage s + 4) is known at compile time: a branch inside
-    // the loop body lets the compiler move a stage's MFMAs past the next
-    // stage's barrier.  The stages of the last partial group of eight fetch no
-    // chunk (there is none after theirs).
-    auto pair = [&](int s, auto chunk) {
-        stage_wait();
-        load_scales(sa, sb, lds, s, wn, wm, c32, hk);
-        mma_stage<0>(acc, lds, s, wn, wm, c32, hk, sa, sb, d, s + 3);
-        stage_wait();
-        if constexpr (decltype(chunk)::value) issue_chunk(s + 4, nk, wsr, xsr, KB, ldxs, lds, wave, lane);
-        mma_stage<1>(acc, lds, s + 1, wn, wm, c32, hk, sa, sb, d, s + 4);
-    };
-    int s = 0;
-    for (; s + 8 <= nk; s += 8) {
-        pair(s, std::true_type{});
-        pair(s + 2, std::false_type{});
-        pair(s + 4, std::false_type{});
-        pair(s + 6, std::false_type{});
-    }
-    for (; s < nk; s += 2) pair(s, std::false_type{});
-    // the last three stages' loads read zeros into unused slots; let them land
-    // before the workgroup's LDS goes away
-    stage_barrier<0>();
-
-    // epilogue: lane holds D[n][m] for m = c32 and n = 8*(e/4) + 4*hk + e%4
-    if constexpr (F32OUT) {
-        // fp32 (256 KB per tile, more than the LDS): 16-byte stores straight from the accumulators
-#pragma unroll
-        for (int tm = 0; tm < 4; ++tm) {
-            const int m = tl.r0 + 128 * wm + 32 * tm + c32;
-            if (m >= tl.r1) continue;
-#pragma unroll
-            for (int tn = 0; tn < 4; ++tn) {
-#pragma unroll
-                for (int qd = 0; qd < 4; ++qd) {
-                    const int n = n0 + 128 * wn + 32 * tn + 8 * qd + 4 * hk;
-                    if (n >= N) continue;
-                    const v16f& v = acc[tn][tm];
-                    float4 o = make_float4(v[4 * qd], v[4 * qd + 1], v[4 * qd + 2], v[4 * qd + 3]);
-                    *reinterpret_cast<float4*>(static_cast<float*>(y) + (int64_t)m * N + n) = o;
-                }
-            }
-        }
-    } else {
-        // bf16: the 256 x 256 tile (128 KB) goes through the LDS ring, free now,
-        // so that each lane stores 16 contiguous bytes and a wave writes two
-        // whole 512-byte row segments per instruction (straight from the
-        // accumulators, each store instruction touched 32 rows).  A row is 32
-        // 16-byte units, XOR-swizzled by the row so that the 8-byte writes of a
-        // wave's 32 rows spread over the banks.
-        constexpr int kRowBytes = kBN * 2;
-        const auto unit_of = [](int m, int u) { return (u ^ m) & 31; };
-#pragma unroll
-        for (int tm = 0; tm < 4; ++tm) {
-            const int m = 128 * wm + 32 * tm + c32;
-#pragma unroll
-            for (int tn = 0; tn < 4; ++tn) {
-#pragma unroll
-                for (int qd = 0; qd < 4; ++qd) {
-                    const int u = (128 * wn + 32 * tn + 8 * qd) / 8;     // 16-byte unit of the row
-                    const v16f& v = acc[tn][tm];
-                    const v2bf16 lo = {(__bf16)v[4 * qd], (__bf16)v[4 * qd + 1]};
-                    const v2bf16 hi = {(__bf16)v[4 * qd + 2], (__bf16)v[4 * qd + 3]};
-                    *reinterpret_cast<uint2*>(lds + m * kRowBytes + unit_of(m, u) * 16 + 8 * hk) =
-                        make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
-                }
-            }
-        }
-        __syncthreads();
-        const int nrows = tl.r1 - tl.r0;
-        const int u = (int)threadIdx.x & 31;
-        const bool col_ok = n0 + 8 * u < N;
-#pragma unroll 4
-        for (int m = (int)threadIdx.x >> 5; m < kBM; m += kThreads / 32) {
-            if (m >= nrows || !col_ok) continue;
-            const uint4 val = *reinterpret_cast<const uint4*>(lds + m * kRowBytes + unit_of(m, u) * 16);
-            *reinterpret_cast<uint4*>(static_cast<uint16_t*>(y) + (int64_t)(tl.r0 + m) * N + n0 + 8 * u) = val;
-        }
-    }
+    // (uniform per workgroup, outside the K loop)
+    if (nrows_x <= 64)
+        tile_product<64, F32OUT>(lds, wr, xr, wsr, xsr, uK, ldx, KB, ldxs, N, K, tl.r0, tl.r1, n0, y);
+    else if (nrows_x <= 128)
+        tile_product<128, F32OUT>(lds, wr, xr, wsr, xsr, uK, ldx, KB, ldxs, N, K, tl.r0, tl.r1, n0, y);
+    else if (nrows_x <= 192)
+        tile_product<192, F32OUT>(lds, wr, xr, wsr, xsr, uK, ldx, KB, ldxs, N, K, tl.r0, tl.r1, n0, y);
+    else
+        tile_product<256, F32OUT>(lds, wr, xr, wsr, xsr, uK, ldx, KB, ldxs, N, K, tl.r0, tl.r1, n0, y);
 }
 
 }  // namespace
