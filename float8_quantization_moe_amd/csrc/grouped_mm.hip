@@ -28,13 +28,14 @@
 //
 // Tile kernel (256 threads = 4 waves; for 256-row tiles in 2 x 2, each wave
 // 128 x 128)
-//   K advances 64 bytes (one MFMA k-step) per stage through a 4-slot LDS ring
-//   of W_g and X tiles (up to 256 rows x 64 B each; 16-byte chunks XOR-swizzled by
-//   row so that the operand reads are free of bank conflicts), filled straight
-//   from global memory by buffer-load-to-LDS.  Each stage waits for its own
-//   loads, reads the wave's operands into VGPRs, and issues its MFMAs with
-//   the loads of the stage three ahead slotted between them; the loop body is
-//   eight stages, one period of the scale-chunk loads.  Global loads use
+//   K advances 128 bytes (two MFMA k-steps) per pair through a 2-slot LDS ring
+//   of W_g and X tiles (up to 256 rows x 128 B each; 16-byte chunks XOR-swizzled
+//   by row so that the operand reads are free of bank conflicts), filled
+//   straight from global memory by buffer-load-to-LDS in whole 128-byte lines.
+//   Each pair waits for its loads, and per k-step reads the wave's operands into
+//   VGPRs and issues its MFMAs, with the next pair's loads slotted between the
+//   first k-step's MFMAs; the loop body is four pairs, one period of the
+//   scale-chunk loads.  Global loads use
 //   raw buffer resources that end at the tile's last valid row: rows past a
 //   group's end or past N read as zero, with no per-row branch.  MFMA operand
 //   A is W_g (output columns), B is X (token rows), so each lane ends up holding
@@ -179,19 +180,22 @@ __global__ __launch_bounds__(kPlanThreads) void mm_plan_kernel(const int32_t* __
 }
 
 // ------------------------------------------------------------ tile kernel ---
-// K advances kBK = 64 bytes (one MFMA k-step) per stage.  Stages live in a
-// 4-deep LDS ring filled by buffer-load-to-LDS (the data never passes through
-// VGPRs), so three stages are in flight while one is multiplied.  Scales
-// travel in chunks of 16 bytes per row (16 k-blocks = 8 stages), fetched seven
-// stages before their first use into a 2-slot ring.
-constexpr int kRing = 4;
-constexpr int kChunkStages = 8;                         // stages per scale chunk
-constexpr int kTileBytes = kBM * kBK;                   // 16 KB of codes per operand per stage
+// K advances 128 bytes per step (a "pair" of MFMA k-steps of 64) through a
+// 2-slot LDS ring filled by buffer-load-to-LDS (the data never passes through
+// VGPRs): each load instruction brings 8 rows x 128 bytes, whole 128-byte
+// lines, and the loads of pair q + 1 go out while pair q is multiplied.  A
+// 4-slot ring of single k-steps (three in flight, each load 16 rows x 64
+// bytes: half lines) kept more bytes in flight, but its loads alone ran 684 us
+// at the MoE configuration against 565 us for the same bytes in whole lines.
+// Scales travel in chunks of 16 bytes per row (16 k-blocks = 4 pairs) into a
+// 2-slot ring.
+constexpr int kPairK = 128;                             // K bytes per ring slot
+constexpr int kSlotBytes = kBM * kPairK;                // 32 KB of codes per operand per slot
 constexpr int kChunkBytes = kBM * 16;                   // 4 KB of scales per operand per chunk
-constexpr int kDataBytes = kRing * 2 * kTileBytes;      // 128 KB
+constexpr int kDataBytes = 2 * 2 * kSlotBytes;          // 128 KB: 2 slots x 2 operands
 constexpr int kDummyBytes = 4 * 1024;                   // sink for loads that carry nothing
 constexpr int kLdsBytes = kDataBytes + 2 * 2 * kChunkBytes + kDummyBytes;   // + 16 KB + 4 KB
-static_assert(kBK == 64 && kChunkStages * kBK == 512, "a scale chunk is 16 k-blocks of 32");
+static_assert(kBK == 64 && kPairK == 2 * kBK && 4 * kPairK == 512, "a scale chunk is 16 k-blocks of 32 = 4 pairs");
 
 typedef __attribute__((address_space(3))) uint8_t* LdsPtr;
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -213,45 +217,38 @@ __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p)
 
 // Buffer load straight into LDS: each lane's `bytes` bytes land at
 // lds + lane * bytes (M0 holds the wave-uniform LDS address).  The load has no
-// VGPR result; its completion is counted by vmcnt, which the stage barrier waits
+// VGPR result; its completion is counted by vmcnt, which the pair barrier waits
 // on explicitly.  Written in asm so that the compiler does not add a
 // conservative wait for it before every later LDS read.  (M0 is reserved by the
 // compiler and set before each of its own uses; nothing else here reads it.)
+// The whole offset is the lane's (VGPR) offset, which the range check covers.
 __device__ __forceinline__ void dma16(const v4i& srd, uint32_t lds, uint32_t voff)
 {
     asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds), "v"(voff), "s"(srd)
                  : "memory");
 }
 
-// Physical 16-byte chunk of logical chunk c in LDS row r (rows of 64 bytes).
-// The fragment reads (lane -> row c32 of a 32-row tile, chunks hk and 2 + hk)
-// measured conflict-free on gfx950 with this swizzle (4 LDS cycles per
-// 128-bit wave read); without it they take 4x as long.
-__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 2) & 3); }
+// Physical 16-byte chunk of logical chunk c (0..7) in LDS row r (rows of 128
+// bytes).  A 128-bit wave read serves 16 lanes at a time; the fragment reads'
+// 16 lanes take 16 consecutive rows at one logical chunk, and with this swizzle
+// they hit 16 different 16-byte bank groups (rows 2j and 2j + 1 share a chunk
+// index but sit in different halves of a 256-byte bank window).
+__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
 
-// Loads of stage t, per wave: its data loads (NL of them: 8 for 256-row tiles,
-// 6 for 128-row tiles) into ring slot t % 4, preceded by 2 scale-chunk loads on
-// the stages that carry a chunk: stage 0 chunk 0, stage 8c + 4 chunk c + 1 (out
-// of range into a sink if that chunk does not exist).  Every stage up to the
-// last + 3 issues its data loads (past the real K they read zeros into a slot
-// nobody reads).  So a stage is NL or NL + 2 loads, and at the top of stage s
-// the loads of stages s+1 and s+2 (2 NL or more) are the only ones that may
-// still be in flight.  (Issuing the chunk loads on every stage,
-// 7 of 8 into the sink, kept the count constant at the price of a fifth more
-// load instructions and LDS writes.)
-__device__ __forceinline__ int scale_chunk_of(int t, int nk)
+// Scale chunks: pair 0 carries chunk 0 and pair 4c + 2 chunk c + 1 (out of
+// range into a sink if that chunk does not exist).
+__device__ __forceinline__ int scale_chunk_of(int p, int np)
 {
-    if (t == 0) return 0;
-    if ((t & 7) == 4 && t + 4 < nk) return (t + 4) >> 3;
+    if (p == 0) return 0;
+    if ((p & 3) == 2 && p + 2 < np) return (p + 2) >> 2;
     return -1;
 }
-__device__ __forceinline__ bool carries_chunk(int t) { return t == 0 || (t & 7) == 4; }
 
 // (KB: bytes per row of the weight scales; ldxs: of the token scales.)
-__device__ __forceinline__ void issue_chunk(int t, int nk, const v4i& wsr, const v4i& xsr, uint32_t KB,
+__device__ __forceinline__ void issue_chunk(int p, int np, const v4i& wsr, const v4i& xsr, uint32_t KB,
                                             uint32_t ldxs, uint8_t* lds, int wave, int lane)
 {
-    const int c = scale_chunk_of(t, nk);
+    const int c = scale_chunk_of(p, np);
     const uint32_t real = lds_addr(lds + kDataBytes + (c & 1) * 2 * kChunkBytes + 64 * 16 * wave);
     const uint32_t sink = lds_addr(lds + kDataBytes + 2 * 2 * kChunkBytes + 1024 * wave);
     const uint32_t row = (uint32_t)(64 * wave + lane);
@@ -272,83 +269,72 @@ struct MmShape {
     static constexpr bool kSquare = BM >= 192;         // 2 x 2 waves (else 4 x 1)
     static constexpr int TN = kSquare ? 4 : 2;         // 32-row W tiles per wave
     static constexpr int TM = kSquare ? BM / 64 : BM / 32;   // 32-row token tiles per wave
-    static constexpr int XL = BM / 64;                 // token-row data loads per wave and stage
-    static constexpr int NL = 4 + XL;                  // data loads per wave and stage (W: 4)
-    static constexpr int NM = TN * TM;                 // MFMAs per wave and stage
+    static constexpr int XL = BM / 32;                 // token-row loads (8 rows each) per wave and pair
+    static constexpr int NL = 8 + XL;                  // data loads per wave and pair (W: 64 rows, 8)
+    static constexpr int NM = TN * TM;                 // MFMAs per wave and k-step
     __device__ static int wn(int wave) { return kSquare ? wave >> 1 : wave; }
     __device__ static int wm(int wave) { return kSquare ? wave & 1 : 0; }
 };
 
-// Per-wave state of the data loads: the lane's offset of load i (rows
-// 64*wave + 16*i .. +15 of W, (BM/4)*wave + 16*i .. of X, its swizzled 16-byte
-// chunk) and the LDS addresses of the wave's first W and X rows in slot 0.
+// Per-wave state of the data loads.  Load i of an operand covers rows
+// base + 8 i .. + 7 (base: 64 wave for W, (BM/4) wave for X), 128 bytes each:
+// lane l takes row base + 8 i + l/8 and physical chunk l % 8, whose logical
+// chunk depends on the row only through i % 2 (base is a multiple of 16), so
+// two lane offsets per operand serve all its loads.
 struct DataLoads {
     v4i wr, xr;
-    uint32_t off[4];          // weight rows (stride K)
-    uint32_t offx[4];         // token rows (stride ldx)
-    uint32_t ldsw, ldsx;
-    int nk;
+    uint32_t offw[2], offx[2];    // lane offsets of the even and odd loads
+    uint32_t sw, sx;              // row strides (bytes) of W and X
+    uint32_t ldsw, ldsx;          // LDS address of the wave's first W and X rows in slot 0
+    int np;
 };
 
-// Data load KL of stage t: W and X loads alternate while both last (W0 X0 W1
+// Data load KL of pair p: W and X loads alternate while both last (W0 X0 W1
 // X1 ...), then the remaining W loads.
 template <int XL, int KL>
-__device__ __forceinline__ void issue_data(const DataLoads& d, int t)
+__device__ __forceinline__ void issue_data(const DataLoads& d, int p)
 {
-    constexpr bool pair = KL < 2 * XL;
-    constexpr int op = pair ? (KL & 1) : 0;
-    constexpr int i = pair ? (KL >> 1) : KL - XL;
-    const uint32_t dst = (op == 0 ? d.ldsw : d.ldsx) + (uint32_t)(t & (kRing - 1)) * 2 * kTileBytes + 16 * i * kBK;
-    const uint32_t off = t < d.nk ? (op == 0 ? d.off[i] : d.offx[i]) + (uint32_t)t * kBK : kOOB;
+    constexpr bool alt = KL < 2 * XL;
+    constexpr int op = alt ? (KL & 1) : 0;
+    constexpr int i = alt ? (KL >> 1) : KL - XL;
+    const uint32_t dst = (op == 0 ? d.ldsw : d.ldsx) + (uint32_t)(p & 1) * 2 * kSlotBytes + 8 * i * kPairK;
+    const uint32_t off = p < d.np ? (op == 0 ? d.offw[i & 1] : d.offx[i & 1]) + (uint32_t)(8 * i) * (op == 0 ? d.sw : d.sx) +
+                                        (uint32_t)p * kPairK
+                                  : kOOB;
     dma16(op == 0 ? d.wr : d.xr, dst, off);
 }
 
 template <int XL, int... KL>
-__device__ __forceinline__ void issue_data_all(const DataLoads& d, int t, std::integer_sequence<int, KL...>)
+__device__ __forceinline__ void issue_data_all(const DataLoads& d, int p, std::integer_sequence<int, KL...>)
 {
-    (issue_data<XL, KL>(d, t), ...);
-}
-
-template <int BM>
-__device__ __forceinline__ void issue_stage(int t, int nk, const v4i& wsr, const v4i& xsr, uint32_t KB,
-                                            uint32_t ldxs, uint8_t* lds, int wave, int lane, const DataLoads& d)
-{
-    using S = MmShape<BM>;
-    if (carries_chunk(t)) issue_chunk(t, nk, wsr, xsr, KB, ldxs, lds, wave, lane);
-    issue_data_all<S::XL>(d, t, std::make_integer_sequence<int, S::NL>{});
+    (issue_data<XL, KL>(d, p), ...);
 }
 
 // Wait until at most N of this wave's buffer loads are outstanding and its LDS
 // reads are done, then meet the other waves.  (No memory fence: a fence would
 // also wait for the loads still meant to be in flight.)
 template <int N>
-__device__ __forceinline__ void stage_barrier()
+__device__ __forceinline__ void pair_barrier()
 {
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-// Top of stage s: its loads (and all older ones) done; stages s+1 and s+2 (at
-// least 2 NL loads) may still be in flight.
-template <int BM>
-__device__ __forceinline__ void stage_wait() { stage_barrier<2 * MmShape<BM>::NL>(); }
-
 // One lane's MFMA operand: logical 16-byte chunks c0 and c1 of LDS row r.
 __device__ __forceinline__ v8i read_frag(const uint8_t* tile, int r, int c0, int c1)
 {
-    const uint4 lo = *reinterpret_cast<const uint4*>(tile + r * kBK + (swz(r, c0) << 4));
-    const uint4 hi = *reinterpret_cast<const uint4*>(tile + r * kBK + (swz(r, c1) << 4));
+    const uint4 lo = *reinterpret_cast<const uint4*>(tile + r * kPairK + (swz(r, c0) << 4));
+    const uint4 hi = *reinterpret_cast<const uint4*>(tile + r * kPairK + (swz(r, c1) << 4));
     v8i v = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
     return v;
 }
 
-// MFMA I of the wave's TN x TM tiles of stage s = 2p + Q, then the data loads
-// of stage t that fall after it.  Lane (c32, hk) holds, of the 64 k of the
-// stage, the bytes k = 16*hk .. +15 and 32 + 16*hk .. +15 (chunks hk and
-// 2 + hk) of its row, and its scale byte covers the 32-k block hk: block
-// 4p + 2Q + hk of the row, which is byte 2Q of the pair's scale word shifted
-// right by 8*hk.  Load j goes after MFMA (2j + 1) NM / (2 NL) (rounded down):
-// with 16 MFMAs and 8 loads, one after every other MFMA (measured 2 % faster
-// than one after each of the first 8, and than all 8 before the MFMAs).
+// MFMA I of the wave's TN x TM tiles in k-step H (0, 1) of a pair, then (in
+// the first k-step) the data loads of the next pair that fall after it.  Lane
+// (c32, hk) holds, of the 64 k of the step, the bytes k = 16*hk .. +15 and
+// 32 + 16*hk .. +15 (logical chunks 4H + hk and 4H + 2 + hk of the pair) of its
+// row, and its scale byte covers the 32-k block hk of the step: block
+// 4p + 2H + hk of the row, which is byte 2H of the pair's scale word shifted
+// right by 8*hk.  Load j goes after MFMA (2j + 1) NM / (2 NL) (rounded down).
 template <int BM, int J>
 __device__ __forceinline__ constexpr int load_slot()
 {
@@ -356,64 +342,63 @@ __device__ __forceinline__ constexpr int load_slot()
 }
 
 template <int BM, int I, int J>
-__device__ __forceinline__ void loads_after(const DataLoads& d, int t)
+__device__ __forceinline__ void loads_after(const DataLoads& d, int p)
 {
     if constexpr (J < MmShape<BM>::NL) {
-        if constexpr (load_slot<BM, J>() == I) issue_data<MmShape<BM>::XL, J>(d, t);
-        loads_after<BM, I, J + 1>(d, t);
+        if constexpr (load_slot<BM, J>() == I) issue_data<MmShape<BM>::XL, J>(d, p);
+        loads_after<BM, I, J + 1>(d, p);
     }
 }
 
-template <int BM, int Q, int I>
+template <int BM, int H, int I>
 __device__ __forceinline__ void mma_step(v16f (&acc)[MmShape<BM>::TN][MmShape<BM>::TM],
                                          const v8i (&a)[MmShape<BM>::TN], const v8i (&b)[MmShape<BM>::TM],
                                          const int (&sa)[MmShape<BM>::TN], const int (&sb)[MmShape<BM>::TM],
-                                         const DataLoads& d, int t)
+                                         const DataLoads& d, int p)
 {
     constexpr int tn = I / MmShape<BM>::TM, tm = I % MmShape<BM>::TM;
-    acc[tn][tm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[tn], b[tm], acc[tn][tm], 0, 0, 2 * Q, sa[tn],
-                                                                  2 * Q, sb[tm]);
-    loads_after<BM, I, 0>(d, t);
+    acc[tn][tm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[tn], b[tm], acc[tn][tm], 0, 0, 2 * H, sa[tn],
+                                                                  2 * H, sb[tm]);
+    if constexpr (H == 0) loads_after<BM, I, 0>(d, p);
     __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int BM, int Q, int... Is>
+template <int BM, int H, int... Is>
 __device__ __forceinline__ void mma_steps(v16f (&acc)[MmShape<BM>::TN][MmShape<BM>::TM],
                                           const v8i (&a)[MmShape<BM>::TN], const v8i (&b)[MmShape<BM>::TM],
                                           const int (&sa)[MmShape<BM>::TN], const int (&sb)[MmShape<BM>::TM],
-                                          const DataLoads& d, int t, std::integer_sequence<int, Is...>)
+                                          const DataLoads& d, int p, std::integer_sequence<int, Is...>)
 {
-    (mma_step<BM, Q, Is>(acc, a, b, sa, sb, d, t), ...);
+    (mma_step<BM, H, Is>(acc, a, b, sa, sb, d, p), ...);
 }
 
-// Stage s = 2p + Q: read its operands from LDS (the wave's W rows from wrow,
-// its token rows from xrow), then issue its MFMAs with the data loads of stage
-// t = s + 3 slotted between them.
-template <int BM, int Q>
-__device__ __forceinline__ void mma_stage(v16f (&acc)[MmShape<BM>::TN][MmShape<BM>::TM], const uint8_t* lds, int s,
+// K-step H of pair q: read its operands from ring slot q % 2 (the wave's W
+// rows from wrow, its token rows from xrow), then issue its MFMAs; in the first
+// step, the data loads of pair p = q + 1 are slotted between them.
+template <int BM, int H>
+__device__ __forceinline__ void mma_kstep(v16f (&acc)[MmShape<BM>::TN][MmShape<BM>::TM], const uint8_t* lds, int q,
                                           int wrow, int xrow, int c32, int hk, const int (&sa)[MmShape<BM>::TN],
-                                          const int (&sb)[MmShape<BM>::TM], const DataLoads& d, int t)
+                                          const int (&sb)[MmShape<BM>::TM], const DataLoads& d, int p)
 {
     using S = MmShape<BM>;
-    const uint8_t* A = lds + (s & (kRing - 1)) * 2 * kTileBytes;
-    const uint8_t* B = A + kTileBytes;
+    const uint8_t* A = lds + (q & 1) * 2 * kSlotBytes;
+    const uint8_t* B = A + kSlotBytes;
     v8i a[S::TN], b[S::TM];
 #pragma unroll
-    for (int i = 0; i < S::TN; ++i) a[i] = read_frag(A, wrow + 32 * i + c32, hk, 2 + hk);
+    for (int i = 0; i < S::TN; ++i) a[i] = read_frag(A, wrow + 32 * i + c32, 4 * H + hk, 4 * H + 2 + hk);
 #pragma unroll
-    for (int i = 0; i < S::TM; ++i) b[i] = read_frag(B, xrow + 32 * i + c32, hk, 2 + hk);
+    for (int i = 0; i < S::TM; ++i) b[i] = read_frag(B, xrow + 32 * i + c32, 4 * H + hk, 4 * H + 2 + hk);
     __builtin_amdgcn_sched_barrier(0);
-    mma_steps<BM, Q>(acc, a, b, sa, sb, d, t, std::make_integer_sequence<int, S::NM>{});
+    mma_steps<BM, H>(acc, a, b, sa, sb, d, p, std::make_integer_sequence<int, S::NM>{});
 }
 
-// Scale words of the pair of stage s (s even) for the lane's W and token
-// tiles: word (s % 8) / 2 of each row's 16-byte chunk, shifted so that byte 2Q
-// is the lane's k-block.
+// Scale words of pair q for the lane's W and token tiles: word q % 4 of each
+// row's 16-byte chunk, shifted so that byte 2H is the lane's k-block.
 template <int BM>
 __device__ __forceinline__ void load_scales(int (&sa)[MmShape<BM>::TN], int (&sb)[MmShape<BM>::TM], const uint8_t* lds,
-                                            int s, int wrow, int xrow, int c32, int hk)
+                                            int q, int wrow, int xrow, int c32, int hk)
 {
-    const uint8_t* sl = lds + kDataBytes + ((s >> 3) & 1) * 2 * kChunkBytes + ((s & 7) >> 1) * 4;
+    const uint8_t* sl = lds + kDataBytes + ((q >> 2) & 1) * 2 * kChunkBytes + (q & 3) * 4;
 #pragma unroll
     for (int i = 0; i < MmShape<BM>::TN; ++i)
         sa[i] = (int)(*reinterpret_cast<const uint32_t*>(sl + (wrow + 32 * i + c32) * 16) >> (8 * hk));
@@ -459,51 +444,51 @@ __device__ __forceinline__ void tile_product(uint8_t* lds, const v4i& wr, const 
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-    // Pipeline: stages 0..2 in flight before the loop; the top of stage s
-    // waits for stage s (loads complete in issue order, and the scale chunk of
-    // s was issued with an earlier stage) and frees slot s-1 for stage s+3.
-    const int nk = K / kBK;                      // even, >= 2
+    // Pipeline: pair 0 is loaded before the loop; the top of pair q waits for
+    // every load issued so far (pair q's, and the scale chunk it needs, issued
+    // with an earlier pair) and meets the other waves, whose reads of slot
+    // (q + 1) % 2 ended with pair q - 1; pair q + 1's loads then go out.
+    const int np = K / kPairK;                   // >= 1
     DataLoads d;
     d.wr = wr;
     d.xr = xr;
-    d.nk = nk;
-    d.ldsw = lds_addr(lds + 64 * wave * kBK);
-    d.ldsx = lds_addr(lds + kTileBytes + (BM / 4) * wave * kBK);
+    d.np = np;
+    d.sw = uK;
+    d.sx = ldx;
+    d.ldsw = lds_addr(lds + 64 * wave * kPairK);
+    d.ldsx = lds_addr(lds + kSlotBytes + (BM / 4) * wave * kPairK);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int row = 64 * wave + 16 * i + (lane >> 2);
-        d.off[i] = (uint32_t)row * uK + ((uint32_t)swz(row, lane & 3) << 4);
-        const int rowx = (BM / 4) * wave + 16 * i + (lane >> 2);
-        d.offx[i] = (uint32_t)rowx * ldx + ((uint32_t)swz(rowx, lane & 3) << 4);
+    for (int par = 0; par < 2; ++par) {
+        const int pc = lane & 7;                                   // physical chunk
+        const int lc = pc ^ ((4 * par + (lane >> 4)) & 7);         // its logical chunk in rows of load parity par
+        d.offw[par] = (uint32_t)(64 * wave + (lane >> 3)) * uK + ((uint32_t)lc << 4);
+        d.offx[par] = (uint32_t)((BM / 4) * wave + (lane >> 3)) * ldx + ((uint32_t)lc << 4);
     }
     int sa[S::TN], sb[S::TM];
-    issue_stage<BM>(0, nk, wsr, xsr, KB, ldxs, lds, wave, lane, d);
-    issue_stage<BM>(1, nk, wsr, xsr, KB, ldxs, lds, wave, lane, d);
-    issue_stage<BM>(2, nk, wsr, xsr, KB, ldxs, lds, wave, lane, d);
-    // Eight stages per iteration, so that which of them fetches a scale chunk
-    // (the second, for stage s + 4) is known at compile time: a branch inside
-    // the loop body lets the compiler move a stage's MFMAs past the next
-    // stage's barrier.  The stages of the last partial group of eight fetch no
-    // chunk (there is none after theirs).
-    auto pair = [&](int s, auto chunk) {
-        stage_wait<BM>();
-        load_scales<BM>(sa, sb, lds, s, wrow, xrow, c32, hk);
-        mma_stage<BM, 0>(acc, lds, s, wrow, xrow, c32, hk, sa, sb, d, s + 3);
-        stage_wait<BM>();
-        if constexpr (decltype(chunk)::value) issue_chunk(s + 4, nk, wsr, xsr, KB, ldxs, lds, wave, lane);
-        mma_stage<BM, 1>(acc, lds, s + 1, wrow, xrow, c32, hk, sa, sb, d, s + 4);
+    issue_chunk(0, np, wsr, xsr, KB, ldxs, lds, wave, lane);
+    issue_data_all<S::XL>(d, 0, std::make_integer_sequence<int, S::NL>{});
+    // Four pairs per iteration, so that which of them fetches a scale chunk
+    // (the second, for pair q + 2) is known at compile time: a branch inside
+    // the loop body lets the compiler move MFMAs past a barrier.  The pairs of
+    // the last partial group of four fetch no chunk (there is none after theirs).
+    auto pair = [&](int q, auto chunk) {
+        pair_barrier<0>();
+        if constexpr (decltype(chunk)::value) issue_chunk(q + 1, np, wsr, xsr, KB, ldxs, lds, wave, lane);
+        load_scales<BM>(sa, sb, lds, q, wrow, xrow, c32, hk);
+        mma_kstep<BM, 0>(acc, lds, q, wrow, xrow, c32, hk, sa, sb, d, q + 1);
+        mma_kstep<BM, 1>(acc, lds, q, wrow, xrow, c32, hk, sa, sb, d, q + 1);
     };
-    int s = 0;
-    for (; s + 8 <= nk; s += 8) {
-        pair(s, std::true_type{});
-        pair(s + 2, std::false_type{});
-        pair(s + 4, std::false_type{});
-        pair(s + 6, std::false_type{});
+    int q = 0;
+    for (; q + 4 <= np; q += 4) {
+        pair(q, std::false_type{});
+        pair(q + 1, std::true_type{});
+        pair(q + 2, std::false_type{});
+        pair(q + 3, std::false_type{});
     }
-    for (; s < nk; s += 2) pair(s, std::false_type{});
-    // the last three stages' loads read zeros into unused slots; let them land
+    for (; q < np; ++q) pair(q, std::false_type{});
+    // the last pair's loads read zeros into the unused slot; let them land
     // before the workgroup's LDS goes away
-    stage_barrier<0>();
+    pair_barrier<0>();
 
     // epilogue: lane holds D[n][m] for m = c32 and n = 8*(e/4) + 4*hk + e%4
     if constexpr (F32OUT) {
