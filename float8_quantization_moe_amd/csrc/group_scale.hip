@@ -14,7 +14,10 @@
 // The amax of a (group, column) must be complete before any element of it is
 // cast, and a 170 MB input re-read right after it was read comes back from HBM
 // at the same rate as a cold read on MI355X (the last-level cache does not turn
-// the second pass into a cheap one).  So the input is read ONCE and held on chip:
+// the second pass into a cheap one).  So the hold method reads the input ONCE
+// and holds it on chip (the default for row-major output, and for column-major
+// output with few groups; with more groups column-major output streams through
+// the two-pass method further down, whose kernels never wait):
 //
 //   plan   build the chunk table and empty-group flags, zero the per-(group,
 //          strip) arrival counters and per-tile "deferred" marks, and fill the
@@ -421,18 +424,18 @@ void group_plan_kernel(const int32_t* __restrict__ offs, int G, int M, int K, Wo
     }
 }
 
+// Size of X from which column-major output holds down to four 128-row blocks
+// per group instead of eight (the method choice below).
+constexpr int64_t kLargeX = (int64_t)512 << 20;
+
 // The groups' clamped ends and 128-row chunk ranges, computed by one wave from
 // the device offsets, for up to kInlineGroups groups (4 per lane: group
 // 64 w + l in window w of lane l): the same clamping and chunk numbering as the
 // plan kernel's tables, so the two-pass amax kernel can do without that launch
 // and leave the tables for the passes after it.
 constexpr int kInlineGroups = 256;
-// Size of X from which column-major output holds down to four 128-row blocks
-// per group instead of eight (the method choice below).
-constexpr int64_t kLargeX = (int64_t)512 << 20;
 struct InlineGroups {
     int e[4], st[4], f[4], n[4];   // end row, start row, first chunk id, chunk count
-    int total;                     // chunks of all groups (ids of rows past the last end follow)
     int last_end;                  // end of the last group
     __device__ void build(const int32_t* __restrict__ offs, int G, int M)
     {
@@ -462,7 +465,6 @@ struct InlineGroups {
             carry_e = readlane(v, kWave - 1);
             carry_f = readlane(incl, kWave - 1);
         }
-        total = carry_f;
         last_end = carry_e;
     }
     // The plan kernel's tables the finalize and column-block passes read: group
