@@ -372,3 +372,22 @@ def test_automatic_method_around_the_large_input_rule(G):
         assert np.array_equal(got_s, want_s), f"layout {layout} scales: {U.first_mismatch(got_s, want_s)}"
         got_q = U.host_u8(qg.t.index_select(1, cols)) if layout == ROW else U.host_u8(qg.t.index_select(0, cols)).T
         assert np.array_equal(got_q, want_q), f"layout {layout} codes: {U.first_mismatch(got_q, want_q)}"
+
+
+@pytest.mark.parametrize("G", [63, 64, 65, 127, 128, 129, 255, 256, 257])
+def test_two_pass_group_tables_at_window_edges(G, group_knobs):
+    """The two-pass method's column-major amax pass finds each tile's group from
+    the offsets with one wave, four groups per lane (windows of 64), for up to
+    256 groups, and writes the tables the later passes read; 257 groups take the
+    plan launch instead.  Group counts at the window edges, with empty groups
+    among ragged ones, both layouts, every byte against the oracle."""
+    group_knobs(method="twopass")
+    M, K = 3000, 136
+    rng = np.random.default_rng(900 + G)
+    sizes = rng.integers(0, 2 * M // G + 1, G)
+    sizes[rng.integers(0, G, max(1, G // 8))] = 0
+    ends = np.minimum(np.cumsum(sizes), M).astype(np.int32)
+    ends[-1] = M
+    x = (rng.standard_normal((M, K)) * np.exp(rng.standard_normal((M, 1)))).astype(np.float32)
+    x_bits = (x.view(np.uint32) >> 16).astype(np.uint16)
+    check_group(x_bits, ends, name=f"G={G}")
