@@ -128,8 +128,8 @@ def grid_hold(M, K, G):            # (128-row chunks + G + 1 slots) x 256-column
     return (_cdiv(M, 128) + G + 1) * _cdiv(K, 256) * 256
 
 
-def grid_finalize(K, G):           # (group, 128-column strip), 256 threads
-    return G * _cdiv(K, 128) * 256
+def grid_finalize(K, G):           # (group, 256-column strip), 256 threads
+    return G * _cdiv(K, 256) * 256
 
 
 def grid_col_blocks(M, K):         # 128-row blocks x 256-column strips, 256 threads

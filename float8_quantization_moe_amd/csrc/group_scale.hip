@@ -941,10 +941,13 @@ void group_amax_kernel(const uint16_t* __restrict__ x, int M, int K, const int32
     }
 }
 
-// One workgroup per (group, strip of 128 columns): lane (cg, rs) reduces
-// partial rows rs, rs + 16, ... of the group for columns 8cg..8cg+7.  An empty
-// group (no chunks) gets the scale of amax 0.
-constexpr int kFThreads = 256, kFW = 128, kFCG = kFW / 8, kFNS = kFThreads / kFCG;
+// One workgroup per (group, strip of 256 columns): lane (cg, rs) reduces
+// partial rows rs, rs + 8, ... of the group for columns 8cg..8cg+7.  An empty
+// group (no chunks) gets the scale of amax 0.  (128-column strips, 16 row
+// slots, ran the G = 128 column-major call about 2 us slower: most groups there
+// have one or two chunks, so most row slots were idle; 512 columns measured the
+// same as 256.)
+constexpr int kFThreads = 256, kFW = 256, kFCG = kFW / 8, kFNS = kFThreads / kFCG;
 __global__ __launch_bounds__(kFThreads)
 void group_finalize_kernel(int K, int SF, Workspace ws, float* __restrict__ scales)
 {
